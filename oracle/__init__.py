@@ -1,0 +1,9 @@
+"""fp64 CPU oracle of the parallel DiT block (test infrastructure only).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It shares no code with the HIP path.
+"""
+from .dit_block import (  # noqa: F401
+    FLAG_NO_GATE, FLAG_NO_RESIDUAL, adaln_ref, attention_ref, block_ref, head_rms_norm,
+    layer_norm, rel_l2, rope4_ref, rope_omega, silu, softmax_rows, stream_index, swiglu_ref,
+    widen_bf16)

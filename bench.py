@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark of the parallel DiT block forward on one MI355X.
+
+A step is one dit_block_fwd over the 1024^2 text-to-image joint sequence
+(4,096 image + 160 text tokens, width 3072, 24 x 128 heads, SwiGLU 9216,
+bf16), with inputs resident in HBM.  Four weight sets (about 1 GB) rotate
+between steps so the 245 MB of one block's weights is not served from the
+256 MB MALL.  Per-stage times come from HIP events the library records on
+the work stream between its kernels.  The fp64 CPU oracle of the same block
+is timed once on the host as a baseline and its output gives the parity of
+the timed configuration.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--weight-sets", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def cpu_baseline(d, cfg):
+    """Time the fp64 oracle on the full block once (one block = one step)."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] + [1])
+        t0 = time.perf_counter()
+        ref = oracle.block_ref(d["x"], d["mod"], d["pos"], d["w_in"], d["w_out"], d["q_scale"],
+                               d["k_scale"], cfg.n_tokens, cfg.n_heads, cfg.head_dim,
+                               cfg.mlp_hidden)
+        sec = time.perf_counter() - t0
+    blas = ",".join(sorted({i.get("internal_api", "?") for i in info})) or "?"
+    return ref, sec, threads, blas
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the block is measured on a single MI355X)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import oracle
+    from flow_matching_diffusion_adaln_amd import configs, inputs, ops, timing
+
+    cfg = configs.CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    ops.load_library()
+    dev_name = torch.cuda.get_device_name(0)
+
+    t_gen = time.perf_counter()
+    d = inputs.make_block_inputs(cfg, seed=0)
+    t_gen = time.perf_counter() - t_gen
+    x = ops.to_device_bf16(d["x"])
+    mod = ops.to_device_bf16(d["mod"])
+    pos = torch.from_numpy(d["pos"]).cuda()
+    qs, ks = ops.to_device_bf16(d["q_scale"]), ops.to_device_bf16(d["k_scale"])
+    weights = [(ops.to_device_bf16(d["w_in"]), ops.to_device_bf16(d["w_out"]))]
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    D, F = cfg.width, cfg.mlp_hidden
+    for _ in range(1, args.weight_sets):
+        w_in = (torch.randn((3 * D + 2 * F, D), generator=gen, device="cuda") * D ** -0.5)
+        w_out = (torch.randn((D, D + F), generator=gen, device="cuda") * (D + F) ** -0.5)
+        weights.append((w_in.to(torch.bfloat16), w_out.to(torch.bfloat16)))
+    desc = ops.make_desc(cfg.n_tokens)
+    ws = ops.alloc_workspace(desc)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(i, events=None):
+        w_in, w_out = weights[i % len(weights)]
+        ops.block_fwd(x, mod, pos, w_in, w_out, qs, ks, desc, y=y, workspace=ws,
+                      stream=stream, events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    n_ev = ops.N_STAGES + 1
+    evs = [timing.create(n_ev) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stage_ms = np.zeros((args.steps, ops.N_STAGES))
+    for i in range(args.steps):
+        for s in range(ops.N_STAGES):
+            stage_ms[i, s] = timing.elapsed_ms(evs[i][s], evs[i][s + 1])
+    block_ms_ev = np.array([timing.elapsed_ms(e[0], e[-1]) for e in evs])
+    for e in evs:
+        timing.destroy(e)
+
+    ms_per_step = wall * 1e3 / args.steps
+    flop = cfg.flop()
+    gemm_in_flop = 2.0 * cfg.N * D * (3 * D + 2 * F)
+    gemm_out_flop = 2.0 * cfg.N * (D + F) * D
+    attn_flop = cfg.attn_flop()
+    st = {name: float(stage_ms[:, i].mean()) for i, name in enumerate(ops.STAGES)}
+    st_med = {name: float(np.median(stage_ms[:, i])) for i, name in enumerate(ops.STAGES)}
+    tflops = flop / (ms_per_step * 1e-3) / 1e12
+    gemm_in_tflops = gemm_in_flop / (st["gemm_in"] * 1e-3) / 1e12
+
+    # parity of this exact configuration (weight set 0) against the oracle
+    step(0)
+    torch.cuda.synchronize()
+    y_set0 = oracle.widen_bf16(ops.to_host_bits(y))
+
+    result = {
+        "metric": "DiT joint-block fwd TFLOP/s & ms/block, 4096 img + 160 txt tokens, bf16",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights; 4 rotating weight sets)",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.description}; width {D}, {cfg.n_heads}x{cfg.head_dim} "
+                        f"heads, SwiGLU {F}, one parallel block forward",
+            "N": cfg.N, "n_tokens": list(cfg.n_tokens), "gflop_per_block": round(flop / 1e9, 2),
+        },
+        "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "block_ms_events_median": round(float(np.median(block_ms_ev)), 4),
+        "stage_ms_mean": {k: round(v, 4) for k, v in st.items()},
+        "stage_ms_median": {k: round(v, 4) for k, v in st_med.items()},
+        "attn": {
+            "ms": round(st["attn"], 4),
+            "tflops": round(attn_flop / (st["attn"] * 1e-3) / 1e12, 2),
+            "frac_mfma_peak": round(attn_flop / (st["attn"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        },
+        "gemm_out_tflops": round(gemm_out_flop / (st["gemm_out"] * 1e-3) / 1e12, 2),
+        "adaln_gbs": round(4.0 * cfg.N * D / (st["adaln"] * 1e-3) / 1e9, 1),
+        "rope_gbs": round(8.0 * cfg.N * D / (st["rope"] * 1e-3) / 1e9, 1),
+        "roofline": {
+            "kernel": "gemm_kernel<EPI_IN> (fused q|k|v|SwiGLU input projection)",
+            "bound": "mfma",
+            "achieved": round(gemm_in_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_in_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "device": dev_name,
+        "input_gen_s": round(t_gen, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        ref, sec, threads, blas = cpu_baseline(d, cfg)
+        result["cpu_baseline"] = {
+            "value": round(flop / sec / 1e12, 5),
+            "unit": "TFLOP/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"one full {cfg.name} block (N={cfg.N}) through oracle.block_ref in numpy "
+                      f"float64, {sec:.2f} s wall, BLAS {blas}, host {cpu_model()}",
+            "seconds_per_block": round(sec, 3),
+        }
+        result["parity"] = {
+            "relL2_y": oracle.rel_l2(y_set0, ref["y"]),
+            "bound": 1e-2,
+        }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

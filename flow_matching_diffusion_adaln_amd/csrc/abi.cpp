@@ -1,0 +1,250 @@
+// C ABI of the DiT block library: host-side validation, workspace layout and
+// the launch sequence of dit_block_fwd.  Every check runs before the first
+// launch, so an error leaves all outputs untouched.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/dit.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool bad_float(float v, bool positive) { return !isfinite(v) || (positive ? v <= 0.f : v < 0.f); }
+
+// Shapes derived from a validated descriptor.
+struct Shape {
+  int N, D, H, F, S, e0, e1;
+};
+
+int check_desc(const dit_block_desc* d, Shape* sh) {
+  if (!d) return DIT_ERR_NULL;
+  if (d->n_streams < 1 || d->n_streams > DIT_MAX_STREAMS) return DIT_ERR_SHAPE;
+  long long n = 0;
+  for (int i = 0; i < d->n_streams; ++i) {
+    if (d->n_tokens[i] < 0) return DIT_ERR_SHAPE;
+    n += d->n_tokens[i];
+  }
+  if (n > DIT_MAX_TOKENS) return DIT_ERR_SHAPE;
+  if (d->n_heads <= 0 || d->head_dim <= 0 || d->width <= 0 || d->mlp_hidden <= 0)
+    return DIT_ERR_SHAPE;
+  if ((long long)d->n_heads * d->head_dim != d->width) return DIT_ERR_SHAPE;
+  if (d->head_dim != DIT_HEAD_DIM) return DIT_ERR_UNSUPPORTED;
+  // GEMM N-tiles are 256 wide and the modulation kernel works in 512-wide rows
+  if (d->n_heads % 4 != 0 || d->width > 8192) return DIT_ERR_UNSUPPORTED;
+  if (d->mlp_hidden % 128 != 0 || d->mlp_hidden > 65536) return DIT_ERR_UNSUPPORTED;
+  if (bad_float(d->rope_theta, true) || bad_float(d->ln_eps, false) || bad_float(d->qk_eps, false))
+    return DIT_ERR_ARG;
+  if (d->flags & ~(DIT_F_NO_RESIDUAL | DIT_F_NO_GATE)) return DIT_ERR_ARG;
+  sh->N = (int)n;
+  sh->D = d->width;
+  sh->H = d->n_heads;
+  sh->F = d->mlp_hidden;
+  sh->S = d->n_streams;
+  sh->e0 = d->n_tokens[0];
+  sh->e1 = sh->e0 + (d->n_streams > 1 ? d->n_tokens[1] : 0);
+  if (d->n_streams == 1) sh->e0 = sh->e1 = (int)n;
+  if (d->n_streams == 2) sh->e1 = (int)n;
+  return DIT_OK;
+}
+
+struct Workspace {
+  uint16_t *u, *q, *k, *v, *cat;
+  size_t bytes;
+};
+
+Workspace layout(const Shape& s, void* base) {
+  const size_t nd = (size_t)s.N * s.D * 2;
+  const size_t ncat = (size_t)s.N * (s.D + s.F) * 2;
+  char* p = static_cast<char*>(base);
+  Workspace w;
+  size_t off = 0;
+  w.u = reinterpret_cast<uint16_t*>(p + off);
+  off += round_up(nd);
+  w.q = reinterpret_cast<uint16_t*>(p + off);
+  off += round_up(nd);
+  w.k = reinterpret_cast<uint16_t*>(p + off);
+  off += round_up(nd);
+  w.v = reinterpret_cast<uint16_t*>(p + off);
+  off += round_up(nd);
+  w.cat = reinterpret_cast<uint16_t*>(p + off);
+  off += round_up(ncat);
+  w.bytes = off;
+  return w;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_ERR_HIP; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const int32_t* pos,
+              const void* w_in, const void* w_out, const void* q_scale, const void* k_scale,
+              void* y, void* workspace, size_t ws_bytes, hipStream_t stream,
+              void* const* events) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc != DIT_OK) return rc;
+  if (s.N == 0) return DIT_OK;
+  if (!x || !mod || !pos || !w_in || !w_out || !q_scale || !k_scale || !y || !workspace)
+    return DIT_ERR_NULL;
+  if (misaligned(x) || misaligned(mod) || misaligned(pos) || misaligned(w_in) ||
+      misaligned(w_out) || misaligned(q_scale) || misaligned(k_scale) || misaligned(y) ||
+      misaligned(workspace))
+    return DIT_ERR_ALIGN;
+  Workspace w = layout(s, workspace);
+  if (ws_bytes < w.bytes) return DIT_ERR_WORKSPACE;
+  if (overlaps(y, (size_t)s.N * s.D * 2, workspace, w.bytes)) return DIT_ERR_ARG;
+  if (events) {
+    for (int i = 0; i <= DIT_N_STAGES; ++i)
+      if (!events[i]) return DIT_ERR_NULL;
+  }
+  auto mark = [&](int i) -> int {
+    if (!events) return DIT_OK;
+    return hip_status(hipEventRecord(static_cast<hipEvent_t>(events[i]), stream));
+  };
+
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* mb = static_cast<const uint16_t*>(mod);
+  if ((rc = mark(DIT_STAGE_ADALN))) return rc;
+  if ((rc = hip_status(dit::launch_adaln(xb, mb, w.u, s.N, s.D, s.e0, s.e1, desc->ln_eps,
+                                         stream))))
+    return rc;
+  if ((rc = mark(DIT_STAGE_GEMM_IN))) return rc;
+  if ((rc = hip_status(dit::launch_gemm_in(w.u, static_cast<const uint16_t*>(w_in), s.N, s.D,
+                                           s.F, w.q, w.k, w.v, w.cat, stream))))
+    return rc;
+  if ((rc = mark(DIT_STAGE_ROPE))) return rc;
+  if ((rc = hip_status(dit::launch_rope4(w.q, w.k, pos, static_cast<const uint16_t*>(q_scale),
+                                         static_cast<const uint16_t*>(k_scale), s.N, s.H,
+                                         desc->rope_theta, desc->qk_eps, stream))))
+    return rc;
+  if ((rc = mark(DIT_STAGE_ATTN))) return rc;
+  if ((rc = hip_status(dit::launch_attn(w.q, w.k, w.v, w.cat, s.N, s.H, s.D, s.D + s.F,
+                                        1.0f / sqrtf((float)DIT_HEAD_DIM), stream))))
+    return rc;
+  if ((rc = mark(DIT_STAGE_GEMM_OUT))) return rc;
+  if ((rc = hip_status(dit::launch_gemm_out(w.cat, static_cast<const uint16_t*>(w_out), s.N,
+                                            s.D, s.F, xb, mb, static_cast<uint16_t*>(y), s.e0,
+                                            s.e1, desc->flags, stream))))
+    return rc;
+  return mark(DIT_N_STAGES);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dit_block_workspace_bytes(const dit_block_desc* desc, size_t* bytes) {
+  Shape s;
+  const int rc = check_desc(desc, &s);
+  if (rc != DIT_OK) return rc;
+  if (!bytes) return DIT_ERR_NULL;
+  *bytes = layout(s, nullptr).bytes;
+  return DIT_OK;
+}
+
+int dit_block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const int32_t* pos,
+                  const void* w_in, const void* w_out, const void* q_scale, const void* k_scale,
+                  void* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return block_fwd(desc, x, mod, pos, w_in, w_out, q_scale, k_scale, y, workspace,
+                   workspace_bytes, stream, nullptr);
+}
+
+int dit_block_fwd_events(const dit_block_desc* desc, const void* x, const void* mod,
+                         const int32_t* pos, const void* w_in, const void* w_out,
+                         const void* q_scale, const void* k_scale, void* y, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, void* const* events) {
+  if (!events) return DIT_ERR_NULL;
+  return block_fwd(desc, x, mod, pos, w_in, w_out, q_scale, k_scale, y, workspace,
+                   workspace_bytes, stream, events);
+}
+
+int dit_attn_fwd(int32_t n_tokens, int32_t n_heads, int32_t head_dim, const void* q,
+                 const void* k, const void* v, void* o, float softmax_scale, hipStream_t stream) {
+  if (n_tokens < 0 || n_tokens > DIT_MAX_TOKENS || n_heads <= 0 || head_dim <= 0)
+    return DIT_ERR_SHAPE;
+  if (head_dim != DIT_HEAD_DIM) return DIT_ERR_UNSUPPORTED;
+  if ((long long)n_heads * head_dim > 65536) return DIT_ERR_UNSUPPORTED;
+  if (bad_float(softmax_scale, true)) return DIT_ERR_ARG;
+  if (n_tokens == 0) return DIT_OK;
+  if (!q || !k || !v || !o) return DIT_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o)) return DIT_ERR_ALIGN;
+  const size_t bytes = (size_t)n_tokens * n_heads * head_dim * 2;
+  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
+    return DIT_ERR_ARG;
+  const int ld = n_heads * head_dim;
+  return hip_status(dit::launch_attn(static_cast<const uint16_t*>(q),
+                                     static_cast<const uint16_t*>(k),
+                                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
+                                     n_tokens, n_heads, ld, ld, softmax_scale, stream));
+}
+
+int rope4_apply(int32_t n_tokens, int32_t n_heads, int32_t head_dim, void* q, void* k,
+                const int32_t* pos, float theta, const void* q_scale, const void* k_scale,
+                float qk_eps, hipStream_t stream) {
+  if (n_tokens < 0 || n_tokens > DIT_MAX_TOKENS || n_heads <= 0 || head_dim <= 0)
+    return DIT_ERR_SHAPE;
+  if (head_dim != DIT_HEAD_DIM) return DIT_ERR_UNSUPPORTED;
+  if ((long long)n_heads * head_dim > 65536) return DIT_ERR_UNSUPPORTED;
+  if (bad_float(theta, true) || bad_float(qk_eps, false)) return DIT_ERR_ARG;
+  if ((q_scale == nullptr) != (k_scale == nullptr)) return DIT_ERR_ARG;
+  if (n_tokens == 0) return DIT_OK;
+  if (!q || !k || !pos) return DIT_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(pos) || misaligned(q_scale) ||
+      misaligned(k_scale))
+    return DIT_ERR_ALIGN;
+  return hip_status(dit::launch_rope4(static_cast<uint16_t*>(q), static_cast<uint16_t*>(k), pos,
+                                      static_cast<const uint16_t*>(q_scale),
+                                      static_cast<const uint16_t*>(k_scale), n_tokens, n_heads,
+                                      theta, qk_eps, stream));
+}
+
+int adaln_mod(int32_t n_streams, const int32_t* n_tokens, int32_t width, const void* x,
+              const void* mod, void* out, float eps, hipStream_t stream) {
+  if (n_streams < 1 || n_streams > DIT_MAX_STREAMS) return DIT_ERR_SHAPE;
+  if (!n_tokens) return DIT_ERR_NULL;
+  long long n = 0;
+  for (int i = 0; i < n_streams; ++i) {
+    if (n_tokens[i] < 0) return DIT_ERR_SHAPE;
+    n += n_tokens[i];
+  }
+  if (n > DIT_MAX_TOKENS || width <= 0) return DIT_ERR_SHAPE;
+  if (width % 512 != 0 || width > 8192) return DIT_ERR_UNSUPPORTED;
+  if (bad_float(eps, false)) return DIT_ERR_ARG;
+  if (n == 0) return DIT_OK;
+  if (!x || !mod || !out) return DIT_ERR_NULL;
+  if (misaligned(x) || misaligned(mod) || misaligned(out)) return DIT_ERR_ALIGN;
+  int e0 = n_tokens[0];
+  int e1 = e0 + (n_streams > 1 ? n_tokens[1] : 0);
+  if (n_streams == 1) e0 = e1 = (int)n;
+  if (n_streams == 2) e1 = (int)n;
+  return hip_status(dit::launch_adaln(static_cast<const uint16_t*>(x),
+                                      static_cast<const uint16_t*>(mod),
+                                      static_cast<uint16_t*>(out), (int)n, width, e0, e1, eps,
+                                      stream));
+}
+
+const char* dit_status_str(int status) {
+  switch (status) {
+    case DIT_OK: return "DIT_OK";
+    case DIT_ERR_NULL: return "DIT_ERR_NULL: a required pointer is null";
+    case DIT_ERR_SHAPE: return "DIT_ERR_SHAPE: inconsistent or out-of-range sizes";
+    case DIT_ERR_UNSUPPORTED: return "DIT_ERR_UNSUPPORTED: size not implemented by this build";
+    case DIT_ERR_ALIGN: return "DIT_ERR_ALIGN: pointer not 16-byte aligned";
+    case DIT_ERR_WORKSPACE: return "DIT_ERR_WORKSPACE: workspace missing or too small";
+    case DIT_ERR_HIP: return "DIT_ERR_HIP: the HIP runtime reported an error";
+    case DIT_ERR_ARG: return "DIT_ERR_ARG: scalar argument out of range or buffers overlap";
+    default: return "DIT_ERR_UNKNOWN";
+  }
+}
+
+}  // extern "C"

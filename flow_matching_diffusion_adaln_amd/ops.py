@@ -1,0 +1,218 @@
+"""ctypes binding of libdit.so (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU, checks
+their dtype, shape and contiguity, and passes raw device pointers and sizes
+to the C ABI declared in include/dit.h.  All computation happens in the HIP
+kernels; if the library is missing the binding raises, there is no fallback.
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+from . import configs
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdit.so")
+
+DIT_F_NO_RESIDUAL = 1
+DIT_F_NO_GATE = 2
+N_STAGES = 5
+STAGES = ("adaln", "gemm_in", "rope", "attn", "gemm_out")
+EXPORTS = ("dit_block_workspace_bytes", "dit_block_fwd", "dit_block_fwd_events", "dit_attn_fwd",
+           "rope4_apply", "adaln_mod", "dit_status_str")
+
+
+class BlockDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_streams", ctypes.c_int32),
+        ("n_tokens", ctypes.c_int32 * 3),
+        ("width", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("mlp_hidden", ctypes.c_int32),
+        ("rope_theta", ctypes.c_float),
+        ("ln_eps", ctypes.c_float),
+        ("qk_eps", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libdit.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    desc_p = ctypes.POINTER(BlockDesc)
+    lib.dit_block_workspace_bytes.argtypes = [desc_p, ctypes.POINTER(sz)]
+    lib.dit_block_fwd.argtypes = [desc_p] + [vp] * 8 + [vp, sz, vp]
+    lib.dit_block_fwd_events.argtypes = [desc_p] + [vp] * 8 + [vp, sz, vp, ctypes.POINTER(vp)]
+    lib.dit_attn_fwd.argtypes = [i32, i32, i32, vp, vp, vp, vp, f32, vp]
+    lib.rope4_apply.argtypes = [i32, i32, i32, vp, vp, vp, f32, vp, vp, f32, vp]
+    lib.adaln_mod.argtypes = [i32, ctypes.POINTER(i32), i32, vp, vp, vp, f32, vp]
+    lib.dit_status_str.argtypes = [ctypes.c_int]
+    lib.dit_status_str.restype = ctypes.c_char_p
+    for name in EXPORTS:
+        if name != "dit_status_str":
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+class DitError(RuntimeError):
+    def __init__(self, rc: int):
+        self.rc = rc
+        super().__init__(load_library().dit_status_str(rc).decode())
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise DitError(rc)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _bf16(t: torch.Tensor, shape, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_desc(n_tokens: Sequence[int], width: int = configs.WIDTH, n_heads: int = configs.N_HEADS,
+              head_dim: int = configs.HEAD_DIM, mlp_hidden: int = configs.MLP_HIDDEN,
+              rope_theta: float = configs.ROPE_THETA, ln_eps: float = configs.LN_EPS,
+              qk_eps: float = configs.QK_EPS, flags: int = 0) -> BlockDesc:
+    d = BlockDesc()
+    d.n_streams = len(n_tokens)
+    for i, n in enumerate(n_tokens):
+        d.n_tokens[i] = int(n)
+    d.width, d.n_heads, d.head_dim, d.mlp_hidden = width, n_heads, head_dim, mlp_hidden
+    d.rope_theta, d.ln_eps, d.qk_eps, d.flags = rope_theta, ln_eps, qk_eps, flags
+    return d
+
+
+def workspace_bytes(desc: BlockDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().dit_block_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def alloc_workspace(desc: BlockDesc, device="cuda") -> torch.Tensor:
+    return torch.empty(max(workspace_bytes(desc), 1), dtype=torch.uint8, device=device)
+
+
+def block_fwd(x, mod, pos, w_in, w_out, q_scale, k_scale, desc: BlockDesc, y=None,
+              workspace=None, stream=None, events=None) -> torch.Tensor:
+    """y = dit_block_fwd(...).  events: optional list of DIT_N_STAGES + 1 raw hipEvent_t."""
+    N = sum(desc.n_tokens[i] for i in range(desc.n_streams))
+    D, F, d = desc.width, desc.mlp_hidden, desc.head_dim
+    _bf16(x, (N, D), "x")
+    _bf16(mod, (desc.n_streams, 3, D), "mod")
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (N, 4) or not pos.is_cuda \
+            or not pos.is_contiguous():
+        raise ValueError("pos must be a contiguous int32 [N, 4] GPU tensor")
+    _bf16(w_in, (3 * D + 2 * F, D), "w_in")
+    _bf16(w_out, (D, D + F), "w_out")
+    _bf16(q_scale, (d,), "q_scale")
+    _bf16(k_scale, (d,), "k_scale")
+    if y is None:
+        y = torch.empty_like(x)
+    _bf16(y, (N, D), "y")
+    if workspace is None:
+        workspace = alloc_workspace(desc, x.device)
+    lib = load_library()
+    args = [ctypes.byref(desc), _ptr(x), _ptr(mod), _ptr(pos), _ptr(w_in), _ptr(w_out),
+            _ptr(q_scale), _ptr(k_scale), _ptr(y), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream)]
+    if events is None:
+        _check(lib.dit_block_fwd(*args))
+    else:
+        arr = (ctypes.c_void_p * (N_STAGES + 1))(*events)
+        _check(lib.dit_block_fwd_events(*args, arr))
+    return y
+
+
+def attn_fwd(q, k, v, o=None, softmax_scale: Optional[float] = None, stream=None):
+    """o = dit_attn_fwd(q, k, v); q, k, v, o bf16 [N, H, d]."""
+    N, H, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _bf16(t, (N, H, d), n)
+    if o is None:
+        o = torch.empty_like(q)
+    _bf16(o, (N, H, d), "o")
+    scale = d ** -0.5 if softmax_scale is None else softmax_scale
+    _check(load_library().dit_attn_fwd(N, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                       ctypes.c_float(scale), _stream(stream)))
+    return o
+
+
+def rope4_apply(q, k, pos, theta: float = configs.ROPE_THETA, q_scale=None, k_scale=None,
+                qk_eps: float = configs.QK_EPS, stream=None):
+    """In place: optional QK RMSNorm, then 4-axis RoPE on q and k ([N, H, d] bf16)."""
+    N, H, d = q.shape
+    _bf16(q, (N, H, d), "q")
+    _bf16(k, (N, H, d), "k")
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (N, 4) or not pos.is_cuda \
+            or not pos.is_contiguous():
+        raise ValueError("pos must be a contiguous int32 [N, 4] GPU tensor")
+    if q_scale is not None:
+        _bf16(q_scale, (d,), "q_scale")
+    if k_scale is not None:
+        _bf16(k_scale, (d,), "k_scale")
+    _check(load_library().rope4_apply(N, H, d, _ptr(q), _ptr(k), _ptr(pos), ctypes.c_float(theta),
+                                      _ptr(q_scale), _ptr(k_scale), ctypes.c_float(qk_eps),
+                                      _stream(stream)))
+    return q, k
+
+
+def adaln_mod(x, mod, n_tokens: Sequence[int], out=None, eps: float = configs.LN_EPS,
+              stream=None):
+    """out = LN(x) * (1 + scale_s) + shift_s per stream; x [N, W] bf16, mod [S, 3, W]."""
+    N, W = x.shape
+    _bf16(x, (N, W), "x")
+    _bf16(mod, (len(n_tokens), 3, W), "mod")
+    if out is None:
+        out = torch.empty_like(x)
+    _bf16(out, (N, W), "out")
+    counts = (ctypes.c_int32 * len(n_tokens))(*[int(n) for n in n_tokens])
+    _check(load_library().adaln_mod(len(n_tokens), counts, W, _ptr(x), _ptr(mod), _ptr(out),
+                                    ctypes.c_float(eps), _stream(stream)))
+    return out
+
+
+def to_device_bf16(bits, device="cuda") -> torch.Tensor:
+    """uint16 bf16 bit patterns (numpy) -> bfloat16 GPU tensor, bytes unchanged."""
+    import numpy as np
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+def to_host_bits(t: torch.Tensor):
+    """bfloat16 GPU tensor -> uint16 numpy bit patterns."""
+    import numpy as np
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

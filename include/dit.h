@@ -1,0 +1,158 @@
+/*
+ * dit.h - C ABI of the MI355X (gfx950) forward of the FLUX.3 Image Klein
+ * parallel DiT block.
+ *
+ * The block (pages: "Welcome FLUX.3 Image Klein in Diffusers", section
+ * "How it works"; the miles page "FLUX 3 Image Klein", sections 1 and 3;
+ * the NeMo AutoModel page, section "Image-Editing LoRA"):
+ *   u  = LN(x) * (1 + scale_s) + shift_s          per-stream AdaLN modulation
+ *   z  = u W_in^T = [q | k | v | gate | up]       to_q, to_k, to_v, ff.linear_in
+ *   q, k <- RoPE4(RMSNorm_head(q|k) * g_q|g_k)    QK norm, 4-axis RoPE (t, h, w, l)
+ *   o  = softmax(q k^T / sqrt(d)) v               full joint attention, no mask
+ *   m  = silu(gate) * up                          SwiGLU, in parallel with attention
+ *   r  = [o | m] W_out^T                          to_out.0 + ff.linear_out
+ *   y  = x + gate_s * r                           gated residual
+ * where s is the stream (image, reference, text) of the token.  Image tokens
+ * carry the modulation of the current timestep t, text and reference tokens
+ * the modulation of t = 0; the modulation vectors themselves are inputs.
+ *
+ * Conventions shared by every call:
+ *   - Tensors are device pointers owned by the caller, row-major, bf16 stored
+ *     as 16-bit patterns unless stated.  They must be 16-byte aligned.
+ *   - Work is enqueued on `stream` (0 = the null stream); calls return once
+ *     enqueued.  The library never allocates, frees or synchronizes, and keeps
+ *     no mutable global state, so calls may come from several threads.
+ *   - Validation runs on the host before any launch; on error nothing is
+ *     launched and outputs are untouched.  Errors are negative status codes,
+ *     and dit_status_str() names them.
+ *   - Token order in a sequence is [image | reference | text]; a call names
+ *     the token count of each segment present, in that order.
+ *   - Supported shapes: head_dim = 128 (4 RoPE axes of 32 dims), width =
+ *     n_heads * 128 with n_heads a multiple of 4 and width at most 8192,
+ *     mlp_hidden a multiple of 128 (at most 65536), at most DIT_MAX_TOKENS
+ *     tokens.  The FLUX.3 Image Klein block is width 3072,
+ *     24 heads, mlp_hidden 9216.
+ *   - A token count of 0 is a valid empty call: DIT_OK, nothing launched.
+ */
+#ifndef DIT_H
+#define DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DIT_OK = 0,
+  DIT_ERR_NULL = -1,        /* a required pointer is null */
+  DIT_ERR_SHAPE = -2,       /* inconsistent sizes (negative counts, H*d != width, too many tokens) */
+  DIT_ERR_UNSUPPORTED = -3, /* a size this build does not implement (head_dim != 128, ...) */
+  DIT_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  DIT_ERR_WORKSPACE = -5,   /* workspace null or smaller than dit_block_workspace_bytes() */
+  DIT_ERR_HIP = -6,         /* the HIP runtime reported a launch error */
+  DIT_ERR_ARG = -7          /* a scalar argument is out of range (eps, theta, flags) */
+};
+
+#define DIT_MAX_STREAMS 3
+#define DIT_MAX_TOKENS 131072
+#define DIT_HEAD_DIM 128
+
+/* flags of dit_block_desc (diagnostics for checking the branch on its own) */
+#define DIT_F_NO_RESIDUAL 1u /* y = gate_s * r            */
+#define DIT_F_NO_GATE 2u     /* the gate is taken as 1     */
+
+/* Stages of dit_block_fwd, in launch order (see dit_block_fwd_events). */
+#define DIT_STAGE_ADALN 0    /* per-stream AdaLN -> u                           */
+#define DIT_STAGE_GEMM_IN 1  /* u W_in^T -> q, k, v and SwiGLU m                */
+#define DIT_STAGE_ROPE 2     /* QK RMSNorm + 4-axis RoPE on q, k                */
+#define DIT_STAGE_ATTN 3     /* joint attention -> o                            */
+#define DIT_STAGE_GEMM_OUT 4 /* [o | m] W_out^T, gated residual -> y            */
+#define DIT_N_STAGES 5
+
+typedef struct dit_block_desc {
+  int32_t n_streams;                 /* 1..3 segments, in [image | reference | text] order */
+  int32_t n_tokens[DIT_MAX_STREAMS]; /* tokens per present segment; N = their sum          */
+  int32_t width;                     /* D, 3072                                            */
+  int32_t n_heads;                   /* H, 24                                              */
+  int32_t head_dim;                  /* d, 128                                             */
+  int32_t mlp_hidden;                /* F, 9216                                            */
+  float rope_theta;                  /* 10000                                              */
+  float ln_eps;                      /* 1e-6, LayerNorm epsilon                            */
+  float qk_eps;                      /* 1e-6, QK RMSNorm epsilon                           */
+  uint32_t flags;                    /* DIT_F_* bits, 0 for the block itself               */
+} dit_block_desc;
+
+/* Bytes of device workspace dit_block_fwd needs for `desc` (about 49 * N * D
+ * bytes at F = 3 D: u, q, k, v and the [o | m] concat buffer, all bf16). */
+int dit_block_workspace_bytes(const dit_block_desc* desc, size_t* bytes);
+
+/* One parallel block forward (the whole chain above).
+ *   x        bf16 [N, D]             input tokens
+ *   mod      bf16 [S, 3, D]          per stream: shift, scale, gate
+ *   pos      int32 [N, 4]            (t, h, w, l) RoPE position of each token
+ *   w_in     bf16 [3D + 2F, D]       rows: to_q | to_k | to_v | linear_in gate | linear_in up
+ *   w_out    bf16 [D, D + F]         columns: to_out.0 (attention) | linear_out (MLP)
+ *   q_scale  bf16 [d], k_scale bf16 [d]   QK RMSNorm scales
+ *   y        bf16 [N, D]             output; y == x (in place) is allowed, any
+ *                                    other overlap between y and an input is not
+ *   workspace device memory of at least dit_block_workspace_bytes(desc)
+ * Rounding: activations between stages are stored as bf16 (round to nearest
+ * even); every sum is accumulated in fp32. */
+int dit_block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const int32_t* pos,
+                  const void* w_in, const void* w_out, const void* q_scale, const void* k_scale,
+                  void* y, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* dit_block_fwd that also records events[i] on `stream` before stage i and
+ * events[DIT_N_STAGES] after the last stage, so the caller can time each
+ * stage with hipEventElapsedTime.  events: host array of DIT_N_STAGES + 1
+ * created hipEvent_t handles. */
+int dit_block_fwd_events(const dit_block_desc* desc, const void* x, const void* mod,
+                         const int32_t* pos, const void* w_in, const void* w_out,
+                         const void* q_scale, const void* k_scale, void* y, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, void* const* events);
+
+/* Full (unmasked) multi-head attention over all N tokens
+ * ("How it works": full attention in the 28 joint blocks; padding attended).
+ *   q, k, v  bf16 [N, H, d]   o  bf16 [N, H, d] (must not overlap q, k, v)
+ *   o[i, h] = sum_j softmax_j(q[i, h] . k[j, h] * softmax_scale) v[j, h]
+ * Online softmax in fp32; the probabilities are rounded to bf16 before the
+ * product with v.  softmax_scale must be finite and > 0 (1/sqrt(d) for the block). */
+int dit_attn_fwd(int32_t n_tokens, int32_t n_heads, int32_t head_dim, const void* q,
+                 const void* k, const void* v, void* o, float softmax_scale, hipStream_t stream);
+
+/* In-place per-head QK RMSNorm (when q_scale and k_scale are both non-null)
+ * followed by 4-axis RoPE on q and k ("How it works": axes t, h, w, l each
+ * own 32 of the 128 head dims; the miles page, section 3: query_norm.scale,
+ * key_norm.scale).
+ *   q, k     bf16 [N, H, d], rotated in place
+ *   pos      int32 [N, 4]   (t, h, w, l)
+ *   Axis a owns dims [32a, 32a + 32); pair j = dims (32a + 2j, 32a + 2j + 1)
+ *   turns by pos_a * theta^(-2j/32): (x, y) -> (x cos - y sin, x sin + y cos).
+ *   RMSNorm: q / sqrt(mean q^2 + qk_eps) * q_scale per head (same for k).
+ * q_scale and k_scale must both be null (no norm) or both be set. */
+int rope4_apply(int32_t n_tokens, int32_t n_heads, int32_t head_dim, void* q, void* k,
+                const int32_t* pos, float theta, const void* q_scale, const void* k_scale,
+                float qk_eps, hipStream_t stream);
+
+/* Per-stream AdaLN modulation ("How it works": shift and scale set
+ * separately per stream, applied to the shared normalized input):
+ *   out[i] = (x[i] - mean) / sqrt(var + eps) * (1 + scale_s) + shift_s
+ * with the biased variance over the row, s the row's stream.
+ *   n_tokens  HOST array of n_streams token counts ([image | reference | text])
+ *   x, out    bf16 [N, width]   (out may equal x)
+ *   mod       bf16 [n_streams, 3, width]; the gate row is not read here
+ * width must be a multiple of 512 and at most 8192. */
+int adaln_mod(int32_t n_streams, const int32_t* n_tokens, int32_t width, const void* x,
+              const void* mod, void* out, float eps, hipStream_t stream);
+
+/* Static name of a status code ("DIT_OK", "DIT_ERR_SHAPE: ...", ...). */
+const char* dit_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_H */

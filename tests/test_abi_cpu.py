@@ -1,0 +1,175 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes its workspace, and rejects bad arguments on the host
+before any launch (every call here fails validation or is an empty call, so
+no kernel is ever enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from flow_matching_diffusion_adaln_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, ARG = 0, -1, -2, -3, -4, -5, -6, -7
+P = 1 << 20       # fake, 16-byte aligned "device" addresses: never dereferenced
+BAD = P + 8       # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        pytest.skip("libdit.so not built")
+    return ops.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(ops.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches_header():
+    # int32 x 8 + float x 3 + uint32 = 48 bytes, no padding
+    assert ctypes.sizeof(ops.BlockDesc) == 48
+
+
+def test_status_strings(lib):
+    for rc in (OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, ARG):
+        s = lib.dit_status_str(rc).decode()
+        assert s.startswith("DIT_OK" if rc == 0 else "DIT_ERR_")
+    assert lib.dit_status_str(-99).decode() == "DIT_ERR_UNKNOWN"
+
+
+def ws(lib, desc):
+    n = ctypes.c_size_t(0)
+    rc = lib.dit_block_workspace_bytes(ctypes.byref(desc), ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_bytes(lib):
+    rc, n = ws(lib, ops.make_desc([4096, 160]))
+    assert rc == OK
+    N, D, F = 4256, 3072, 9216
+    assert n >= 2 * (4 * N * D + N * (D + F))
+    assert n < 2 * (4 * N * D + N * (D + F)) + 5 * 256
+    rc, n8352 = ws(lib, ops.make_desc([4096, 4096, 160]))
+    assert rc == OK and n8352 > 400e6
+    assert ws(lib, ops.make_desc([0]))[0] == OK
+
+
+@pytest.mark.parametrize("field,value,want", [
+    ("n_streams", 0, SHAPE), ("n_streams", 4, SHAPE),
+    ("head_dim", 64, SHAPE),            # 24 x 64 != 3072
+    ("width", 3000, SHAPE),
+    ("n_heads", 0, SHAPE),
+    ("mlp_hidden", 9200, UNSUP),
+    ("rope_theta", 0.0, ARG), ("ln_eps", -1.0, ARG), ("qk_eps", float("nan"), ARG),
+    ("flags", 4, ARG),
+])
+def test_desc_validation(lib, field, value, want):
+    d = ops.make_desc([4096, 160])
+    setattr(d, field, value)
+    assert ws(lib, d)[0] == want
+
+
+def test_desc_head_dim_and_tokens(lib):
+    d = ops.make_desc([256, 80], width=6 * 64, n_heads=6, head_dim=64)
+    assert ws(lib, d)[0] == UNSUP          # head_dim 64 is not implemented
+    d = ops.make_desc([256, 80], width=2 * 128, n_heads=2)
+    assert ws(lib, d)[0] == UNSUP          # heads must come in multiples of 4
+    d = ops.make_desc([-1, 80])
+    assert ws(lib, d)[0] == SHAPE
+    d = ops.make_desc([131072, 1])
+    assert ws(lib, d)[0] == SHAPE          # above DIT_MAX_TOKENS
+    assert lib.dit_block_workspace_bytes(None, ctypes.byref(ctypes.c_size_t())) == NULL
+
+
+def fwd(lib, desc, ptrs=None, ws_bytes=None, events=None):
+    p = [P] * 9 if ptrs is None else ptrs
+    if ws_bytes is None:
+        ws_bytes = ws(lib, desc)[1]
+    args = [ctypes.byref(desc)] + [ctypes.c_void_p(v) if v else None for v in p] + \
+        [ctypes.c_size_t(ws_bytes), None]
+    if events is None:
+        return lib.dit_block_fwd(*args)
+    return lib.dit_block_fwd_events(*args, events)
+
+
+def test_block_fwd_host_errors(lib):
+    d = ops.make_desc([256, 80])
+    for i in range(9):
+        p = [P + (1 << 30) * j for j in range(9)]
+        p[i] = 0
+        assert fwd(lib, d, p) == NULL, i
+    for i in range(9):
+        p = [P + (1 << 30) * j for j in range(9)]
+        p[i] = BAD + (1 << 30) * i
+        assert fwd(lib, d, p) == ALIGN, i
+    p = [P + (1 << 30) * j for j in range(9)]
+    assert fwd(lib, d, p, ws_bytes=ws(lib, d)[1] - 1) == WS
+    # y overlapping the workspace
+    p[8] = p[7]
+    assert fwd(lib, d, p) == ARG
+    # events array required by the events variant, and each event non-null
+    p = [P + (1 << 30) * j for j in range(9)]
+    ev = (ctypes.c_void_p * 6)(*([1] * 5 + [0]))
+    assert fwd(lib, d, p, events=ev) == NULL
+
+
+def test_empty_block_is_a_noop(lib):
+    d = ops.make_desc([0, 0])
+    assert fwd(lib, d, [0] * 9, ws_bytes=0) == OK
+
+
+def test_attn_host_errors(lib):
+    c = ctypes.c_void_p
+    f = lib.dit_attn_fwd
+    a, b, cc, o = c(P), c(P + (1 << 30)), c(P + (2 << 30)), c(P + (3 << 30))
+    assert f(100, 24, 64, a, b, cc, o, 0.1, None) == UNSUP
+    assert f(-1, 24, 128, a, b, cc, o, 0.1, None) == SHAPE
+    assert f(100, 0, 128, a, b, cc, o, 0.1, None) == SHAPE
+    assert f(100, 24, 128, None, b, cc, o, 0.1, None) == NULL
+    assert f(100, 24, 128, c(BAD), b, cc, o, 0.1, None) == ALIGN
+    assert f(100, 24, 128, a, b, cc, o, 0.0, None) == ARG
+    assert f(100, 24, 128, a, b, cc, o, float("inf"), None) == ARG
+    assert f(100, 24, 128, a, b, cc, c(P + 4096), 0.1, None) == ARG   # o overlaps q
+    assert f(0, 24, 128, None, None, None, None, 0.1, None) == OK      # empty call
+
+
+def test_rope_host_errors(lib):
+    c = ctypes.c_void_p
+    f = lib.rope4_apply
+    q, k, pos, g = c(P), c(P + (1 << 30)), c(P + (2 << 30)), c(P + (3 << 30))
+    assert f(10, 24, 96, q, k, pos, 1e4, None, None, 1e-6, None) == UNSUP
+    assert f(10, 24, 128, q, k, pos, 1e4, g, None, 1e-6, None) == ARG
+    assert f(10, 24, 128, q, k, pos, -1.0, None, None, 1e-6, None) == ARG
+    assert f(10, 24, 128, None, k, pos, 1e4, None, None, 1e-6, None) == NULL
+    assert f(10, 24, 128, q, k, c(BAD), 1e4, None, None, 1e-6, None) == ALIGN
+    assert f(0, 24, 128, None, None, None, 1e4, None, None, 1e-6, None) == OK
+
+
+def test_adaln_host_errors(lib):
+    c = ctypes.c_void_p
+    f = lib.adaln_mod
+    n2 = (ctypes.c_int32 * 2)(256, 80)
+    x, m, o = c(P), c(P + (1 << 30)), c(P + (2 << 30))
+    assert f(0, n2, 3072, x, m, o, 1e-6, None) == SHAPE
+    assert f(2, None, 3072, x, m, o, 1e-6, None) == NULL
+    assert f(2, n2, 3000, x, m, o, 1e-6, None) == UNSUP
+    assert f(2, n2, 16384, x, m, o, 1e-6, None) == UNSUP
+    assert f(2, n2, 3072, x, None, o, 1e-6, None) == NULL
+    assert f(2, n2, 3072, x, m, c(BAD), 1e-6, None) == ALIGN
+    assert f(2, n2, 3072, x, m, o, -1.0, None) == ARG
+    bad = (ctypes.c_int32 * 2)(256, -80)
+    assert f(2, bad, 3072, x, m, o, 1e-6, None) == SHAPE
+    empty = (ctypes.c_int32 * 2)(0, 0)
+    assert f(2, empty, 3072, None, None, None, 1e-6, None) == OK

@@ -75,8 +75,13 @@ __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a));
 
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[2][BN * BK];
+  // Four distinct LDS arrays (not one indexed array) so the compiler can see
+  // that fragment reads of one stage never alias the direct-to-LDS loads in
+  // flight into the other, and does not wait on those loads before reading.
+  __shared__ __attribute__((aligned(16))) uint16_t s_a0[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b0[BN * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a1[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b1[BN * BK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -97,21 +102,25 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   // the lane fetches.  Wave w fills rows [64 w, 64 w + 64) of both tiles.
   const int lrow = lane >> 3;                  // row inside the 8-row slab
   const int lch = (lane & 7) ^ lrow;           // logical chunk this lane fetches
+  // byte offsets in 32 bits: the loads then use the scalar-base + vector-offset form
   uint32_t aoff[8], boff[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = wave * 64 + 8 * j + lrow;
     const int arow = min(tm * BM + r, g.M - 1);
-    aoff[j] = (uint32_t)arow * (uint32_t)g.K + lch * 8;
-    boff[j] = (uint32_t)weight_row<EPI>(g, tn, r) * (uint32_t)g.K + lch * 8;
+    aoff[j] = ((uint32_t)arow * (uint32_t)g.K + lch * 8) * 2u;
+    boff[j] = ((uint32_t)weight_row<EPI>(g, tn, r) * (uint32_t)g.K + lch * 8) * 2u;
   }
-  auto gload = [&](int kt, int st) {
-    const uint32_t ko = kt * BK;
+  const char* abase = reinterpret_cast<const char*>(g.A);
+  const char* bbase = reinterpret_cast<const char*>(g.W);
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  auto gload = [&](int kt, uint16_t* sa, uint16_t* sb) {
+    const uint32_t ko = (uint32_t)kt * (BK * 2);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int slab = (wave * 64 + 8 * j) * BK;
-      __builtin_amdgcn_global_load_lds(g.A + aoff[j] + ko, (__attribute__((address_space(3))) void*)&s_a[st][slab], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(g.W + boff[j] + ko, (__attribute__((address_space(3))) void*)&s_b[st][slab], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(abase + (aoff[j] + ko), (lds_ptr)(sa + slab), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bbase + (boff[j] + ko), (lds_ptr)(sb + slab), 16, 0, 0);
     }
   };
 
@@ -123,37 +132,85 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = g.K / BK;
-  gload(0, 0);
-  wait_vm();
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1, cur ^ 1);
-    const uint16_t* sa = s_a[cur];
-    const uint16_t* sb = s_b[cur];
+  const int KT = g.K / BK;  // even for every supported shape
+  // MFMA fragments, double-buffered in registers: while the 16 MFMAs of one
+  // 16-wide k step run, the 8 fragment reads of the next step are in flight.
+  bf16x8 fa[2][4], fb[2][4];
+  auto read_frags = [&](const uint16_t* sa, const uint16_t* sb, int ks, int slot) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 128 + i * 32 + ln;
-        af[i] = *reinterpret_cast<const bf16x8*>(sa + r * BK + (((2 * ks + hl) ^ (r & 7)) << 3));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wn * 128 + j * 32 + ln;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + r * BK + (((2 * ks + hl) ^ (r & 7)) << 3));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + ln;
+      fa[slot][i] = *reinterpret_cast<const bf16x8*>(&sa[r * BK + (((2 * ks + hl) ^ (r & 7)) << 3)]);
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn * 128 + j * 32 + ln;
+      fb[slot][j] = *reinterpret_cast<const bf16x8*>(&sb[r * BK + (((2 * ks + hl) ^ (r & 7)) << 3)]);
+    }
+  };
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+  };
+  // One k tile: compute from (ca, cb) while the next tile streams into (na, nb).
+  // The last tile reloads itself into the idle buffer, which is never read;
+  // that keeps the body free of branches.  The instruction order is pinned:
+  // the compiler would otherwise sink the global loads next to the wait at
+  // the end of the tile (no overlap) and pair each fragment read with its
+  // first use.  Each 16-wide k step issues its 16 MFMAs (512 cycles)
+  // interleaved with the next step's 8 fragment reads; the first step also
+  // carries the 16 direct-to-LDS loads of the next tile.
+  auto ktile = [&](int kt, const uint16_t* ca, const uint16_t* cb, uint16_t* na, uint16_t* nb) {
+    gload(min(kt + 1, KT - 1), na, nb);
+    read_frags(ca, cb, 1, 1);
+    mfmas(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // 2 VMEM loads
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(ca, cb, 2, 0);
+    mfmas(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(ca, cb, 3, 1);
+    mfmas(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+    __builtin_amdgcn_sched_barrier(0);
     wait_vm();
     __syncthreads();
+    read_frags(na, nb, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  gload(0, s_a0, s_b0);
+  wait_vm();
+  __syncthreads();
+  read_frags(s_a0, s_b0, 0, 0);
+  for (int kt = 0; kt < KT; kt += 2) {
+    ktile(kt, s_a0, s_b0, s_a1, s_b1);
+    ktile(kt + 1, s_a1, s_b1, s_a0, s_b0);
   }
 
   // Epilogue.  Lane holds C[8 rr + 4 hl + j][ln] of each 32 x 32 block in

@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--weight-sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the timed steps "
+                         "(reference point for the profiler's FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -110,6 +113,14 @@ def main():
         w_in, w_out = weights[i % len(weights)]
         ops.block_fwd(x, mod, pos, w_in, w_out, qs, ks, desc, y=y, workspace=ws,
                       stream=stream, events=events)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for i in range(args.warmup):
         step(i)

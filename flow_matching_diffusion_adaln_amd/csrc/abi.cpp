@@ -11,6 +11,7 @@
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr long long kMaxBytes = 1ll << 32;
 
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -39,6 +40,10 @@ int check_desc(const dit_block_desc* d, Shape* sh) {
   // GEMM N-tiles are 256 wide and the modulation kernel works in 512-wide rows
   if (d->n_heads % 4 != 0 || d->width > 8192) return DIT_ERR_UNSUPPORTED;
   if (d->mlp_hidden % 128 != 0 || d->mlp_hidden > 65536) return DIT_ERR_UNSUPPORTED;
+  // kernels address tensors with 32-bit byte offsets
+  const long long width = d->width, hidden = d->mlp_hidden;
+  if (n * (width + hidden) * 2 >= kMaxBytes || (3 * width + 2 * hidden) * width * 2 >= kMaxBytes)
+    return DIT_ERR_UNSUPPORTED;
   if (bad_float(d->rope_theta, true) || bad_float(d->ln_eps, false) || bad_float(d->qk_eps, false))
     return DIT_ERR_ARG;
   if (d->flags & ~(DIT_F_NO_RESIDUAL | DIT_F_NO_GATE)) return DIT_ERR_ARG;
@@ -174,6 +179,7 @@ int dit_attn_fwd(int32_t n_tokens, int32_t n_heads, int32_t head_dim, const void
     return DIT_ERR_SHAPE;
   if (head_dim != DIT_HEAD_DIM) return DIT_ERR_UNSUPPORTED;
   if ((long long)n_heads * head_dim > 65536) return DIT_ERR_UNSUPPORTED;
+  if ((long long)n_tokens * n_heads * head_dim * 2 >= kMaxBytes) return DIT_ERR_UNSUPPORTED;
   if (bad_float(softmax_scale, true)) return DIT_ERR_ARG;
   if (n_tokens == 0) return DIT_OK;
   if (!q || !k || !v || !o) return DIT_ERR_NULL;

@@ -5,21 +5,29 @@
 // prompt padding included) and the miles page "FLUX 3 Image Klein", section 3
 // (the DiT takes no padding mask).  No mask is applied.
 //
-// Design (gfx950, 64-wide waves, 32x32x16 bf16 MFMA):
+// Design (gfx950, 64-wide waves, 32x32x16 bf16 MFMA, 64-bank LDS):
 //  * A workgroup is one head x 128 queries; each of its 4 waves owns 32
 //    queries for the whole key loop.  Keys stream through LDS in tiles of 64,
-//    double-buffered, loaded once per workgroup and shared by the 4 waves.
+//    double-buffered; K and V go from HBM/L2 straight into LDS with the
+//    16-byte direct-to-LDS loads, no staging registers.
 //  * Scores are computed transposed, S^T = K Q^T (A = K from LDS, B = Q held
 //    in registers).  In the 32x32 MFMA result a lane holds one column, so
-//    each lane owns one query: the row max and row sum of the softmax are
-//    in-lane reductions plus one exchange with the other half-wave.
-//  * The K rows fed to the A operand are permuted (key_slot below) so that
-//    the 16 scores a lane ends up holding are exactly the 16 keys it must
-//    supply as the B operand of O^T = V^T P^T.  P never leaves registers.
-//  * V is stored transposed in LDS (V^T[dim][key]) while staging, so the
-//    A operand V^T reads 16 contiguous bytes per lane.
-//  * Online softmax in fp32 with exp2 (scale * log2 e folded into one FMA),
-//    P rounded to bf16 for the MFMA, one division by the row sum at the end.
+//    each lane owns one query: row max and row sum are in-lane reductions
+//    plus one exchange with the other half-wave.
+//  * The K rows fed to the A operand are permuted (key_slot) so that the 16
+//    scores a lane holds are exactly the 16 keys it supplies as the B operand
+//    of O^T = V^T P^T.  P never leaves registers.
+//  * V stays row-major [key][dim] in LDS; the A operand V^T of the PV MFMA is
+//    read with gfx950's transposing LDS read (ds_read_b64_tr_b16): each lane
+//    fetches 4 dims of one key and the hardware hands every lane 4 keys of one
+//    dim.
+//  * Online softmax in fp32 with the hardware exp2 (v_exp_f32; results below
+//    2^-126 flush to zero, far under bf16 resolution of P), scale * log2 e
+//    folded into one FMA.
+//    The running max is only moved (and O, l rescaled) when a row's max grows
+//    by more than 2^8; otherwise the stale max is kept, which bounds P by 2^8
+//    and leaves the result unchanged (P and l share the same reference).  P is
+//    rounded to bf16 for the MFMA; one division by the row sum at the end.
 //  * Workgroups of one head are kept on one XCD so its K and V stay in that
 //    XCD's L2.
 #include "common.h"
@@ -29,14 +37,26 @@ namespace dit {
 
 namespace {
 
-constexpr int BQ = 128;  // queries per workgroup
-constexpr int BKEY = 64; // keys per tile
-constexpr int HD = 128;  // head dim
+constexpr int BQ = 128;   // queries per workgroup
+constexpr int BKEY = 64;  // keys per tile
+constexpr int HD = 128;   // head dim
+constexpr float RESCALE_LOG2 = 8.f;
 
-// K tile in LDS: [64 keys][128 dims], 16 chunks of 16 B per row, chunk index
-// xor-swizzled so the permuted-row A reads and the row-wise stores are
-// conflict free.
-__device__ __forceinline__ int kswz(int row) { return (row & 3) | ((row >> 1) & 4); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+
+// gfx950's LDS has 64 banks of 4 B; a 16-byte access serves 16 lanes per
+// cycle (256 B), an 8-byte one 32 lanes.
+// K tile [64 keys][128 dims], rows of 256 B = 16 chunks of 16 B: the 16 lanes
+// of an A read hit 16 different rows at one logical chunk, so the chunk is
+// xor-ed with the row's low 4 bits.
+__device__ __forceinline__ int kswz(int row) { return row & 15; }
+// V tile [64 keys][128 dims], rows of 256 B = 4 segments of 64 B (32 dims):
+// a 32-lane half of a transposing read touches 4 consecutive rows at one
+// segment, so the segment is xor-ed with the row's low 2 bits.
+__device__ __forceinline__ int vswz(int row) { return row & 3; }
 
 // Key held by A-operand row m of a 32-key block (m = 8r + 4h + j maps to
 // 16(r/2) + 8h + 4(r%2) + j): with this order the MFMA output register
@@ -47,11 +67,7 @@ __device__ __forceinline__ int key_slot(int m) {
   return 16 * (r >> 1) + 8 * h + 4 * (r & 1) + j;
 }
 
-// 16-bit element e (0..7) of a 16-byte vector, zero-extended
-__device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
-  const uint32_t d = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
-  return (e & 1) ? (d >> 16) : (d & 0xffffu);
-}
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace
 
@@ -61,8 +77,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
                                                           uint16_t* __restrict__ o, int N,
                                                           int H, int ld_qkv, int ld_o,
                                                           float c) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][BKEY * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][HD * BKEY];
+  // distinct arrays per stage: reads of one stage never wait on the
+  // direct-to-LDS loads in flight into the other
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0[BKEY * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v0[BKEY * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k1[BKEY * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v1[BKEY * HD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, hl = lane >> 5;
@@ -70,87 +90,86 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   const int id = xcd_remap(blockIdx.x, nqt * H);
   const int h = id / nqt, qt = id % nqt;
   const int q0 = qt * BQ + wave * 32;
-  const size_t hoff = (size_t)h * HD;
 
   // Q fragments (B operand of S^T = K Q^T): lane holds q[q0 + ln][16 s + 8 hl .. + 8]
   bf16x8 qf[8];
   {
     const int qi = min(q0 + ln, N - 1);
-    const uint4* qp = reinterpret_cast<const uint4*>(q + (size_t)qi * ld_qkv + hoff);
+    const uint4* qp = reinterpret_cast<const uint4*>(q + (size_t)qi * ld_qkv + (size_t)h * HD);
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, qp[2 * s + hl]);
   }
+
+  // Direct-to-LDS loads: a wave instruction fills 1 KB = 4 rows of 256 B;
+  // lane i lands in row 4 j' + i / 16 at physical chunk i % 16.  Wave w
+  // fills rows [16 w, 16 w + 16) of both tiles.
+  const char* kbase = reinterpret_cast<const char*>(k + (size_t)h * HD);
+  const char* vbase = reinterpret_cast<const char*>(v + (size_t)h * HD);
+  const int prow = lane >> 4, pch = lane & 15;
+  uint32_t kch[4], vch[4];  // byte offset of the chunk this lane fetches, per slab
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = wave * 16 + 4 * j + prow;
+    kch[j] = (uint32_t)((pch ^ kswz(r)) * 16);
+    vch[j] = (uint32_t)(((((pch >> 2) ^ vswz(r)) << 2) | (pch & 3)) * 16);
+  }
+  const uint32_t row_bytes = (uint32_t)ld_qkv * 2u;
+  auto dma = [&](int t, uint16_t* sk, uint16_t* sv) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wave * 16 + 4 * j + prow;
+      const uint32_t key = (uint32_t)min(t * BKEY + r, N - 1);
+      const int slab = (wave * 16 + 4 * j) * HD;
+      __builtin_amdgcn_global_load_lds(kbase + (key * row_bytes + kch[j]), (lds_ptr)(sk + slab), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + (key * row_bytes + vch[j]), (lds_ptr)(sv + slab), 16, 0, 0);
+    }
+  };
+
+  // per-lane LDS read offsets (bytes) that do not change from tile to tile
+  const int krow = key_slot(ln);  // + 32 kb
+  uint32_t koff[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) koff[st] = krow * 256 + (((2 * st + hl) ^ kswz(krow)) << 4);
+  // transposing V read: 16-lane group g covers dims 16 (g & 1) .. + 15 of the
+  // 32-dim block and keys 8 (g >> 1) + 4 u .. + 3 of the 16-key step (u = 0, 1);
+  // lane i of the group reads key (i >> 2), dims 4 (i & 3) .. + 3
+  const int g = lane >> 4, gi = lane & 15;
+  const int vrow = 8 * (g >> 1) + (gi >> 2);
+  uint32_t voff[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    voff[d] = vrow * 256 + ((d ^ vswz(vrow)) << 6) + (16 * (g & 1) + 4 * (gi & 3)) * 2;
 
   f32x16 acc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;  // running max, already multiplied by c
+  float l_run = 0.f;
 
-  // staging: K chunk (row = id >> 4, chunk = id & 15) for id = tid + 256 i;
-  // V: 4 consecutive keys (group u) x 8 dims (chunk cv) per thread
-  const int vu = tid & 15, vc = tid >> 4;
-  uint4 kreg[4], vreg[4];
   const int ntiles = (N + BKEY - 1) / BKEY;
+  const bool ragged = (N % BKEY) != 0;
 
-  auto gload = [&](int t) {
-    const int key0 = t * BKEY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
-      const int key = min(key0 + (idx >> 4), N - 1);
-      kreg[i] = *reinterpret_cast<const uint4*>(k + (size_t)key * ld_qkv + hoff + (idx & 15) * 8);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int key = min(key0 + 4 * vu + kk, N - 1);
-      vreg[kk] = *reinterpret_cast<const uint4*>(v + (size_t)key * ld_qkv + hoff + vc * 8);
-    }
-  };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx >> 4, ch = idx & 15;
-      *reinterpret_cast<uint4*>(&s_k[st][row * HD + ((ch ^ kswz(row)) << 3)]) = kreg[i];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t lo = half16(vreg[0], e) | (half16(vreg[1], e) << 16);
-      const uint32_t hi = half16(vreg[2], e) | (half16(vreg[3], e) << 16);
-      const int row = 8 * vc + e;  // dim
-      const int ch = (vu >> 1) ^ (row & 7);
-      *reinterpret_cast<uint2*>(&s_vt[st][row * BKEY + ch * 8 + (vu & 1) * 4]) = make_uint2(lo, hi);
-    }
-  };
+  auto tile = [&](int t, const uint16_t* sk, const uint16_t* sv, uint16_t* nk, uint16_t* nv) {
+    // the last tile reloads itself into the idle buffer (never read)
+    dma(min(t + 1, ntiles - 1), nk, nv);
+    const char* skb = reinterpret_cast<const char*>(sk);
+    const char* svb = reinterpret_cast<const char*>(sv);
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
-
-    // S^T = K Q^T for two 32-key blocks
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int row = 32 * kb + key_slot(ln);
-      const uint16_t* kr = &s_k[cur][row * HD];
-      const int sw = kswz(row);
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + (((2 * st + hl) ^ sw) << 3));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(skb + kb * 32 * 256 + koff[st]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
       }
     }
 
-    // keys past N (last tile only) get no weight
-    if ((t + 1) * BKEY > N) {
+    if (ragged && t == ntiles - 1) {  // keys past N get no weight
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -165,11 +184,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f((m_run - m_new) * c);
-    const float mc = m_new * c;
-    m_run = m_new;
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    if (__any(mx > m_run + RESCALE_LOG2)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+    }
 
     bf16x8 pb[4];
     float psum = 0.f;
@@ -177,37 +202,42 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(fmaf(s[kb][r], c, -mc));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_run));
         psum += p;
         pb[2 * kb + (r >> 3)][r & 7] = (__bf16)p;
       }
-    l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+    l_run += psum;
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T; the A operand (8 keys of one dim) is two transposing reads
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const int row = 32 * d + ln;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            &s_vt[cur][row * BKEY + (((2 * ks + hl) ^ (row & 7)) << 3)]);
-        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], acc[d], 0, 0, 0);
+        const char* base = svb + ks * 16 * 256 + voff[d];
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(base));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(base + 4 * 256));
+        const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[ks],
+                                                         acc[d], 0, 0, 0);
       }
     }
-
-    if (t + 1 < ntiles) sstore(cur ^ 1);
+    wait_vm();
     __syncthreads();
+  };
+
+  dma(0, s_k0, s_v0);
+  wait_vm();
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, s_k0, s_v0, s_k1, s_v1);
+    if (t + 1 < ntiles) tile(t + 1, s_k1, s_v1, s_k0, s_v0);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
   const int qi = q0 + ln;
   if (qi < N) {
-    uint16_t* op = o + (size_t)qi * ld_o + hoff;
+    uint16_t* op = o + (size_t)qi * ld_o + (size_t)h * HD;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll

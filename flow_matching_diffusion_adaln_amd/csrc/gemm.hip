@@ -18,8 +18,7 @@
 // wave 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32
 // accumulators per lane).  A and W tiles are staged through LDS, double
 // buffered (2 x 64 KB), with the 16-byte chunk index xor-swizzled by the row
-// so both the row-wise stores and the MFMA fragment reads are bank-conflict
-// free.  Tiles are ordered XCD-aware: each XCD takes one contiguous range of
+// so the MFMA fragment reads are bank-conflict free.  Tiles are ordered XCD-aware: each XCD takes one contiguous range of
 // tiles, walked in groups of 4 N-tiles so the A and W panels in flight on one
 // XCD stay few and L2-resident.
 #include "common.h"
@@ -67,6 +66,13 @@ __device__ __forceinline__ int weight_row(const GemmArgs& g, int tn, int r) {
   return tn * BN + r;
 }
 
+// LDS tiles are rows of 64 bf16 (128 B = 8 chunks of 16 B).  gfx950's LDS has
+// 64 banks of 4 B, so 16 lanes of a 16-byte read are served per cycle: the
+// 16 consecutive rows one MFMA fragment read touches must land on 16
+// distinct 16-byte bank slots.  Row r covers slots 8 (r % 2) .. + 7, so the
+// chunk is xor-ed with (r >> 1) & 7, a bijection on the 8 rows of each parity.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
 // Wait for this wave's outstanding vector-memory operations, including the
 // direct-to-LDS loads, before the barrier that publishes the tile.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -98,15 +104,15 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   // Global -> LDS with gfx950's 16-byte direct loads (no staging registers).
   // One wave instruction fills 1 KB of LDS = 8 tile rows of 128 B; lane i
   // lands in row 8 j' + i / 8 at physical chunk i % 8, which holds logical
-  // chunk (i % 8) ^ (row & 7) of the swizzled layout, so that is the chunk
+  // chunk (i % 8) ^ swz(row) of the swizzled layout, so that is the chunk
   // the lane fetches.  Wave w fills rows [64 w, 64 w + 64) of both tiles.
   const int lrow = lane >> 3;                  // row inside the 8-row slab
-  const int lch = (lane & 7) ^ lrow;           // logical chunk this lane fetches
   // byte offsets in 32 bits: the loads then use the scalar-base + vector-offset form
   uint32_t aoff[8], boff[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = wave * 64 + 8 * j + lrow;
+    const int lch = (lane & 7) ^ swz(r);       // logical chunk this lane fetches
     const int arow = min(tm * BM + r, g.M - 1);
     aoff[j] = ((uint32_t)arow * (uint32_t)g.K + lch * 8) * 2u;
     boff[j] = ((uint32_t)weight_row<EPI>(g, tn, r) * (uint32_t)g.K + lch * 8) * 2u;
@@ -140,12 +146,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 128 + i * 32 + ln;
-      fa[slot][i] = *reinterpret_cast<const bf16x8*>(&sa[r * BK + (((2 * ks + hl) ^ (r & 7)) << 3)]);
+      fa[slot][i] = *reinterpret_cast<const bf16x8*>(&sa[r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = wn * 128 + j * 32 + ln;
-      fb[slot][j] = *reinterpret_cast<const bf16x8*>(&sb[r * BK + (((2 * ks + hl) ^ (r & 7)) << 3)]);
+      fb[slot][j] = *reinterpret_cast<const bf16x8*>(&sb[r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
     }
   };
   auto mfmas = [&](int slot) {

@@ -30,7 +30,8 @@
  *   - Supported shapes: head_dim = 128 (4 RoPE axes of 32 dims), width =
  *     n_heads * 128 with n_heads a multiple of 4 and width at most 8192,
  *     mlp_hidden a multiple of 128 (at most 65536), at most DIT_MAX_TOKENS
- *     tokens.  The FLUX.3 Image Klein block is width 3072,
+ *     tokens, and every tensor (including the [N, D + F] internal buffer)
+ *     under 4 GiB; larger calls return DIT_ERR_UNSUPPORTED.  The FLUX.3 Image Klein block is width 3072,
  *     24 heads, mlp_hidden 9216.
  *   - A token count of 0 is a valid empty call: DIT_OK, nothing launched.
  */

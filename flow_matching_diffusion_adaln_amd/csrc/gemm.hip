@@ -14,13 +14,16 @@
 //    and ff.linear_out summed, with y = x + gate_s * r in the epilogue (one
 //    gate per stream, "How it works": scale, shift and gate per stream).
 //
-// Tiling for gfx950: 256 x 256 x 64 workgroup tile, 4 waves in 2 x 2, each
-// wave 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32
-// accumulators per lane).  A and W tiles are staged through LDS, double
-// buffered (2 x 64 KB), with the 16-byte chunk index xor-swizzled by the row
-// so the MFMA fragment reads are bank-conflict free.  Tiles are ordered XCD-aware: each XCD takes one contiguous range of
-// tiles, walked in groups of 4 N-tiles so the A and W panels in flight on one
-// XCD stay few and L2-resident.
+// Tiling for gfx950: 256 x 256 workgroup tile, 4 waves in 2 x 2, each wave
+// 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32
+// accumulators per lane, held in AGPRs).  The K loop streams 32-wide k tiles
+// from L2/HBM straight into LDS with 16-byte direct-to-LDS loads through a
+// 4-stage ring (4 x 32 KB): loads run three tiles ahead of the MFMAs, which
+// hides the L2-miss latency that a double buffer exposes.  The 16-byte chunk
+// index is xor-swizzled by the row so fragment reads are bank-conflict free.
+// Tiles are ordered XCD-aware: each XCD takes one contiguous range of tiles,
+// walked in groups of 4 N-tiles so the A and W panels in flight on one XCD
+// stay few and L2-resident.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,7 +31,11 @@ namespace dit {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int STAGES = 4;            // LDS ring depth; loads run STAGES - 1 tiles ahead
+constexpr int CH = BK / 8;           // 16-byte chunks per tile row (4)
+constexpr int RPI = 64 / CH;         // tile rows filled by one 1 KB wave load (16)
+constexpr int NLD = BM / RPI / 4;    // loads per wave per tile, for each of A and W (4)
 constexpr int GROUP_N = 4;
 
 enum { EPI_IN = 0, EPI_OUT = 1 };
@@ -66,28 +73,42 @@ __device__ __forceinline__ int weight_row(const GemmArgs& g, int tn, int r) {
   return tn * BN + r;
 }
 
-// LDS tiles are rows of 64 bf16 (128 B = 8 chunks of 16 B).  gfx950's LDS has
+// LDS tiles are rows of 32 bf16 (64 B = 4 chunks of 16 B).  gfx950's LDS has
 // 64 banks of 4 B, so 16 lanes of a 16-byte read are served per cycle: the
 // 16 consecutive rows one MFMA fragment read touches must land on 16
-// distinct 16-byte bank slots.  Row r covers slots 8 (r % 2) .. + 7, so the
-// chunk is xor-ed with (r >> 1) & 7, a bijection on the 8 rows of each parity.
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// distinct 16-byte bank slots.  Row r covers slots 4 (r % 4) .. + 3, so the
+// chunk is xor-ed with (r >> 2) & 3, a bijection on the 4 rows of each class.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
-// Wait for this wave's outstanding vector-memory operations, including the
-// direct-to-LDS loads, before the barrier that publishes the tile.
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt left alone
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+constexpr int LGKMCNT0 = 0xC07F;
+
+// Workgroup barrier for the K loop.  __syncthreads() would also wait for every
+// outstanding vector-memory operation (the whole prefetch ring); here the
+// caller waits only for the tile about to be read, plus its own LDS reads.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
-  // Four distinct LDS arrays (not one indexed array) so the compiler can see
-  // that fragment reads of one stage never alias the direct-to-LDS loads in
-  // flight into the other, and does not wait on those loads before reading.
-  __shared__ __attribute__((aligned(16))) uint16_t s_a0[BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b0[BN * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t s_a1[BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b1[BN * BK];
+  // One LDS array per ring stage (A tile, then W tile), not one indexed array:
+  // the compiler tracks direct-to-LDS stores per LDS variable, so it can see
+  // that fragment reads of one stage never alias the loads in flight into the
+  // others and does not wait on them.  (It tracks only a few variables, hence
+  // A and W share one array per stage.)
+  __shared__ __attribute__((aligned(16))) uint16_t s_st0[(BM + BN) * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_st1[(BM + BN) * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_st2[(BM + BN) * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_st3[(BM + BN) * BK];
+  uint16_t* const ring[STAGES] = {s_st0, s_st1, s_st2, s_st3};
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -102,17 +123,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   const int tn = grp * GROUP_N + rem % gw;
 
   // Global -> LDS with gfx950's 16-byte direct loads (no staging registers).
-  // One wave instruction fills 1 KB of LDS = 8 tile rows of 128 B; lane i
-  // lands in row 8 j' + i / 8 at physical chunk i % 8, which holds logical
-  // chunk (i % 8) ^ swz(row) of the swizzled layout, so that is the chunk
-  // the lane fetches.  Wave w fills rows [64 w, 64 w + 64) of both tiles.
-  const int lrow = lane >> 3;                  // row inside the 8-row slab
+  // One wave instruction fills 1 KB of LDS = 16 tile rows of 64 B; lane i
+  // lands in row 16 j' + i / 4 at physical chunk i % 4, which holds logical
+  // chunk (i % 4) ^ swz(row) of the swizzled layout, so that is the chunk the
+  // lane fetches.  Wave w fills rows [64 w, 64 w + 64) of both tiles.
+  const int lrow = lane / CH;
   // byte offsets in 32 bits: the loads then use the scalar-base + vector-offset form
-  uint32_t aoff[8], boff[8];
+  uint32_t aoff[NLD], boff[NLD];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = wave * 64 + 8 * j + lrow;
-    const int lch = (lane & 7) ^ swz(r);       // logical chunk this lane fetches
+  for (int j = 0; j < NLD; ++j) {
+    const int r = wave * (NLD * RPI) + RPI * j + lrow;
+    const int lch = (lane % CH) ^ swz(r);
     const int arow = min(tm * BM + r, g.M - 1);
     aoff[j] = ((uint32_t)arow * (uint32_t)g.K + lch * 8) * 2u;
     boff[j] = ((uint32_t)weight_row<EPI>(g, tn, r) * (uint32_t)g.K + lch * 8) * 2u;
@@ -120,13 +141,16 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   const char* abase = reinterpret_cast<const char*>(g.A);
   const char* bbase = reinterpret_cast<const char*>(g.W);
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  auto gload = [&](int kt, uint16_t* sa, uint16_t* sb) {
-    const uint32_t ko = (uint32_t)kt * (BK * 2);
+  const int KT = g.K / BK;  // a multiple of STAGES for every supported shape
+  // tile kt -> ring stage st; past the end the last tile is reloaded into the
+  // idle stage (never read), so the loop needs no branches
+  auto gload = [&](int kt, uint16_t* st) __attribute__((always_inline)) {
+    const uint32_t ko = (uint32_t)min(kt, KT - 1) * (BK * 2);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int slab = (wave * 64 + 8 * j) * BK;
-      __builtin_amdgcn_global_load_lds(abase + (aoff[j] + ko), (lds_ptr)(sa + slab), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(bbase + (boff[j] + ko), (lds_ptr)(sb + slab), 16, 0, 0);
+    for (int j = 0; j < NLD; ++j) {
+      const int slab = (wave * (NLD * RPI) + RPI * j) * BK;
+      __builtin_amdgcn_global_load_lds(abase + (aoff[j] + ko), (lds_ptr)(st + slab), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bbase + (boff[j] + ko), (lds_ptr)(st + BM * BK + slab), 16, 0, 0);
     }
   };
 
@@ -138,141 +162,140 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = g.K / BK;  // even for every supported shape
   // MFMA fragments, double-buffered in registers: while the 16 MFMAs of one
   // 16-wide k step run, the 8 fragment reads of the next step are in flight.
   bf16x8 fa[2][4], fb[2][4];
-  auto read_frags = [&](const uint16_t* sa, const uint16_t* sb, int ks, int slot) {
+  auto read_frags = [&](const uint16_t* st, int ks, int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 128 + i * 32 + ln;
-      fa[slot][i] = *reinterpret_cast<const bf16x8*>(&sa[r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
+      fa[slot][i] = *reinterpret_cast<const bf16x8*>(&st[r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = wn * 128 + j * 32 + ln;
-      fb[slot][j] = *reinterpret_cast<const bf16x8*>(&sb[r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
+      fb[slot][j] = *reinterpret_cast<const bf16x8*>(&st[BM * BK + r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
     }
   };
-  auto mfmas = [&](int slot) {
+  auto mfmas = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0);
   };
-  // One k tile: compute from (ca, cb) while the next tile streams into (na, nb).
-  // The last tile reloads itself into the idle buffer, which is never read;
-  // that keeps the body free of branches.  The instruction order is pinned:
-  // the compiler would otherwise sink the global loads next to the wait at
-  // the end of the tile (no overlap) and pair each fragment read with its
-  // first use.  Each 16-wide k step issues its 16 MFMAs (512 cycles)
-  // interleaved with the next step's 8 fragment reads; the first step also
-  // carries the 16 direct-to-LDS loads of the next tile.
-  auto ktile = [&](int kt, const uint16_t* ca, const uint16_t* cb, uint16_t* na, uint16_t* nb) {
-    gload(min(kt + 1, KT - 1), na, nb);
-    read_frags(ca, cb, 1, 1);
+  // One k tile from ring stage s.  The instruction order is pinned (the
+  // compiler would otherwise sink the loads next to the waits and pair each
+  // fragment read with its first use): the first k step interleaves its 16
+  // MFMAs with the 8 loads of the tile STAGES - 1 ahead and the 8 fragment
+  // reads of the second step.
+  auto ktile = [&](int kt, int s) __attribute__((always_inline)) {
+    gload(kt + STAGES - 1, ring[(s + STAGES - 1) % STAGES]);
+    read_frags(ring[s], 1, 1);
     mfmas(0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // 2 VMEM loads
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global load
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
     }
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(ca, cb, 2, 0);
-    mfmas(1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(ca, cb, 3, 1);
-    mfmas(0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(1);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm();
-    __syncthreads();
-    read_frags(na, nb, 0, 0);
+    // tile kt + 1 must have landed; the STAGES - 2 younger tiles may still fly
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NLD * (STAGES - 2)));
+    __builtin_amdgcn_s_waitcnt(LGKMCNT0);
+    ring_barrier();
+    read_frags(ring[(s + 1) % STAGES], 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  gload(0, s_a0, s_b0);
-  wait_vm();
-  __syncthreads();
-  read_frags(s_a0, s_b0, 0, 0);
-  for (int kt = 0; kt < KT; kt += 2) {
-    ktile(kt, s_a0, s_b0, s_a1, s_b1);
-    ktile(kt + 1, s_a1, s_b1, s_a0, s_b0);
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) gload(s, ring[s]);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NLD * (STAGES - 2)));
+  ring_barrier();
+  read_frags(ring[0], 0, 0);
+  for (int kt = 0; kt < KT; kt += STAGES) {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) ktile(kt + s, s);
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  // Epilogue.  Lane holds C[8 rr + 4 hl + j][ln] of each 32 x 32 block in
-  // register 4 rr + j.
+  // Epilogue.  The MFMAs compute C^T (weights as the A operand), so in block
+  // (i, j) lane (ln, hl) holds output row i*32 + ln and the 4 consecutive
+  // columns j*32 + 8 rr + 4 hl .. + 3 in registers 4 rr .. 4 rr + 3: every
+  // store, residual load and gate load is 8 contiguous bytes.
   const int row_base = tm * BM + wm * 128;
+  const int col_base = tn * BN + wn * 128 + 4 * hl;
+  auto pack4 = [](float a, float b, float c, float d) __attribute__((always_inline)) {
+    return make_uint2(pack2(a, b), pack2(c, d));
+  };
   if (EPI == EPI_IN) {
     const int n_qkv = 3 * g.D / BN;
     if (tn < n_qkv) {
+      // q | k | v: 4 consecutive columns never straddle a D boundary
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = tn * BN + wn * 128 + j * 32 + ln;
-        const int which = col / g.D;
-        const int cc = col - which * g.D;
-        uint16_t* dst = which == 0 ? g.q : which == 1 ? g.k : g.v;
+      for (int i = 0; i < 4; ++i) {
+        const int row = row_base + i * 32 + ln;
+        if (row >= g.M) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = row_base + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (row < g.M)
-              dst[(size_t)row * g.D + cc] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][r]);
+          for (int rr = 0; rr < 4; ++rr) {
+            const int col = col_base + j * 32 + 8 * rr;
+            const int which = col / g.D;
+            uint16_t* dst = which == 0 ? g.q : which == 1 ? g.k : g.v;
+            const f32x16& a = acc[i][j];
+            *reinterpret_cast<uint2*>(dst + (size_t)row * g.D + (col - which * g.D)) =
+                pack4(a[4 * rr], a[4 * rr + 1], a[4 * rr + 2], a[4 * rr + 3]);
           }
       }
     } else {
+      // SwiGLU: block 2p holds gate, block 2p + 1 up, of the same hidden units
       const int ldc = g.D + g.F;
+      const int hid_base = (tn - n_qkv) * 128 + wn * 64 + 4 * hl;
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int hidden = (tn - n_qkv) * 128 + wn * 64 + p * 32 + ln;
+      for (int i = 0; i < 4; ++i) {
+        const int row = row_base + i * 32 + ln;
+        if (row >= g.M) continue;
+        uint16_t* dst = g.cat + (size_t)row * ldc + g.D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int p = 0; p < 2; ++p)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = row_base + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            const float mval = silu(acc[i][2 * p][r]) * acc[i][2 * p + 1][r];
-            if (row < g.M)
-              g.cat[(size_t)row * ldc + g.D + hidden] = __builtin_bit_cast(uint16_t, (__bf16)mval);
+          for (int rr = 0; rr < 4; ++rr) {
+            const f32x16& ga = acc[i][2 * p];
+            const f32x16& up = acc[i][2 * p + 1];
+            float m[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m[e] = silu(ga[4 * rr + e]) * up[4 * rr + e];
+            *reinterpret_cast<uint2*>(dst + hid_base + p * 32 + 8 * rr) = pack4(m[0], m[1], m[2], m[3]);
           }
       }
     }
   } else {
     const bool use_gate = !(g.flags & 2u), use_res = !(g.flags & 1u);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = tn * BN + wn * 128 + j * 32 + ln;
+    for (int i = 0; i < 4; ++i) {
+      const int row = row_base + i * 32 + ln;
+      if (row >= g.M) continue;
+      const uint16_t* gate = g.mod + (size_t)stream_of(row, g.e0, g.e1) * 3 * g.D + 2 * g.D;
+      const uint16_t* xr = g.x + (size_t)row * g.D;
+      uint16_t* yr = g.y + (size_t)row * g.D;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row_base + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (row < g.M) {
-            const int s = stream_of(row, g.e0, g.e1);
-            const float gate = use_gate ? bf2f(g.mod[(size_t)s * 3 * g.D + 2 * g.D + col]) : 1.f;
-            const float res = use_res ? bf2f(g.x[(size_t)row * g.D + col]) : 0.f;
-            g.y[(size_t)row * g.D + col] =
-                __builtin_bit_cast(uint16_t, (__bf16)fmaf(gate, acc[i][j][r], res));
-          }
+        for (int rr = 0; rr < 4; ++rr) {
+          const int col = col_base + j * 32 + 8 * rr;
+          const uint2 gv = use_gate ? *reinterpret_cast<const uint2*>(gate + col) : make_uint2(0x3f803f80u, 0x3f803f80u);
+          const uint2 xv = use_res ? *reinterpret_cast<const uint2*>(xr + col) : make_uint2(0u, 0u);
+          const f32x16& a = acc[i][j];
+          *reinterpret_cast<uint2*>(yr + col) =
+              pack4(fmaf(lo2f(gv.x), a[4 * rr], lo2f(xv.x)), fmaf(hi2f(gv.x), a[4 * rr + 1], hi2f(xv.x)),
+                    fmaf(lo2f(gv.y), a[4 * rr + 2], lo2f(xv.y)), fmaf(hi2f(gv.y), a[4 * rr + 3], hi2f(xv.y)));
         }
     }
   }

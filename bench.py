@@ -44,6 +44,25 @@ def parse():
     return ap.parse_args()
 
 
+def measured_traffic():
+    """HBM bytes per launch of the input-projection GEMM from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (copy-calibrated), or None when the
+    GEMM source has changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_in_c2_traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "flow_matching_diffusion_adaln_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != rec.get("source_sha256_16"):
+        return None
+    return rec.get("traffic_bytes_per_dispatch")
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -195,7 +214,9 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_in_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
+            "traffic_unit": "bytes per launch",
+            "algorithmic": f"{gemm_in_flop / 1e9:.1f} GFLOP per launch = 2 N D (3D + 2F)",
         },
         "device": dev_name,
         "input_gen_s": round(t_gen, 1),

@@ -244,7 +244,7 @@ const char* dit_status_str(int status) {
     case DIT_OK: return "DIT_OK";
     case DIT_ERR_NULL: return "DIT_ERR_NULL: a required pointer is null";
     case DIT_ERR_SHAPE: return "DIT_ERR_SHAPE: inconsistent or out-of-range sizes";
-    case DIT_ERR_UNSUPPORTED: return "DIT_ERR_UNSUPPORTED: size not implemented by this build";
+    case DIT_ERR_UNSUPPORTED: return "DIT_ERR_UNSUPPORTED: size this library does not implement";
     case DIT_ERR_ALIGN: return "DIT_ERR_ALIGN: pointer not 16-byte aligned";
     case DIT_ERR_WORKSPACE: return "DIT_ERR_WORKSPACE: workspace missing or too small";
     case DIT_ERR_HIP: return "DIT_ERR_HIP: the HIP runtime reported an error";

@@ -50,7 +50,7 @@ enum {
   DIT_OK = 0,
   DIT_ERR_NULL = -1,        /* a required pointer is null */
   DIT_ERR_SHAPE = -2,       /* inconsistent sizes (negative counts, H*d != width, too many tokens) */
-  DIT_ERR_UNSUPPORTED = -3, /* a size this build does not implement (head_dim != 128, ...) */
+  DIT_ERR_UNSUPPORTED = -3, /* a size this library does not implement (head_dim != 128, ...) */
   DIT_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
   DIT_ERR_WORKSPACE = -5,   /* workspace null or smaller than dit_block_workspace_bytes() */
   DIT_ERR_HIP = -6,         /* the HIP runtime reported a launch error */

@@ -22,7 +22,7 @@ What is computed, step by step (sources are the pages' sections):
 * Full attention with no mask, padding attended: same section and the miles
   page, section 3 (the DiT takes no padding mask).
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
   norm = LayerNorm without affine, biased variance, eps 1e-6;
   u = LN(x) * (1 + scale) + shift; one gate per stream on the summed branch;
   no biases; W_in rows [q | k | v | gate | up]; silu on the gate half;

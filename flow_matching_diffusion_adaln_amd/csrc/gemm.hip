@@ -110,7 +110,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t s_st3[(BM + BN) * BK];
   uint16_t* const ring[STAGES] = {s_st0, s_st1, s_st2, s_st3};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar: LDS addresses of the direct loads (M0) then come
+  // from scalar arithmetic instead of a v_readfirstlane per load
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int ln = lane & 31, hl = lane >> 5;
 
@@ -186,9 +189,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   };
   // One k tile from ring stage s.  The instruction order is pinned (the
   // compiler would otherwise sink the loads next to the waits and pair each
-  // fragment read with its first use): the first k step interleaves its 16
+  // fragment read with its first use).  The first k step interleaves its 16
   // MFMAs with the 8 loads of the tile STAGES - 1 ahead and the 8 fragment
-  // reads of the second step.
+  // reads of the second step.  The barrier then comes before the second k
+  // step, whose fragments are already in registers: the next tile's first
+  // fragment reads overlap those 16 MFMAs instead of stalling after the
+  // barrier.  That is safe because every read of stage s has completed before
+  // the barrier (lgkmcnt(0)), and stage s is refilled only after it.
   auto ktile = [&](int kt, int s) __attribute__((always_inline)) {
     gload(kt + STAGES - 1, ring[(s + STAGES - 1) % STAGES]);
     read_frags(ring[s], 1, 1);
@@ -204,13 +211,18 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
     }
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
-    __builtin_amdgcn_sched_barrier(0);
     // tile kt + 1 must have landed; the STAGES - 2 younger tiles may still fly
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NLD * (STAGES - 2)));
     __builtin_amdgcn_s_waitcnt(LGKMCNT0);
     ring_barrier();
     read_frags(ring[(s + 1) % STAGES], 0, 0);
+    mfmas(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 

@@ -5,7 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/dit.h"
+#include "dit.h"
 #include "kernels.h"
 
 namespace {

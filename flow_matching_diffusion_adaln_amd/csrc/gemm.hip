@@ -14,11 +14,14 @@
 //    and ff.linear_out summed, with y = x + gate_s * r in the epilogue (one
 //    gate per stream, "How it works": scale, shift and gate per stream).
 //
-// Tiling for gfx950: 256 x 256 workgroup tile, 4 waves in 2 x 2, each wave
-// 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32
-// accumulators per lane, held in AGPRs).  The K loop streams 32-wide k tiles
-// from L2/HBM straight into LDS with 16-byte direct-to-LDS loads through a
-// 4-stage ring (4 x 32 KB): loads run three tiles ahead of the MFMAs, which
+// Tiling for gfx950: BM x 256 workgroup tiles with BM = 256 (4 waves in
+// 2 x 2, 128 x 128 each) or BM = 224 (4 waves in 1 x 4, 224 x 64 each), built
+// from v_mfma_f32_32x32x16_bf16 blocks with the fp32 accumulators in AGPRs.
+// The host picks the tile height: fewest rounds of tiles over the CUs, then
+// the shorter tile (224 divides the 4,256-token sequence into 19 tiles, 256
+// leaves a 160-row remainder).  The K loop streams 32-wide k
+// tiles from L2/HBM straight into LDS with 16-byte direct-to-LDS loads
+// through a 4-stage ring: loads run three tiles ahead of the MFMAs, which
 // hides the L2-miss latency that a double buffer exposes.  The 16-byte chunk
 // index is xor-swizzled by the row so fragment reads are bank-conflict free.
 // Tiles are ordered XCD-aware: each XCD takes one contiguous range of tiles,
@@ -31,11 +34,11 @@ namespace dit {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int BN = 256, BK = 32;
 constexpr int STAGES = 4;            // LDS ring depth; loads run STAGES - 1 tiles ahead
 constexpr int CH = BK / 8;           // 16-byte chunks per tile row (4)
 constexpr int RPI = 64 / CH;         // tile rows filled by one 1 KB wave load (16)
-constexpr int NLD = BM / RPI / 4;    // loads per wave per tile, for each of A and W (4)
+constexpr int NLD = 4;               // loads per wave per k tile, for each of A and W
 constexpr int GROUP_N = 4;
 
 enum { EPI_IN = 0, EPI_OUT = 1 };
@@ -58,17 +61,32 @@ struct GemmArgs {
   uint32_t flags;
 };
 
+// Tile geometry: BM rows, WM x WN waves, MB x NB blocks of 32 x 32 per wave.
+template <int BM_>
+struct Tile {
+  static constexpr int BM = BM_;
+  static constexpr int WM = BM_ == 256 ? 2 : 1;
+  static constexpr int WN = 4 / WM;
+  static constexpr int MB = BM_ / (32 * WM);
+  static constexpr int NB = BN / (32 * WN);
+  static constexpr int A_SLABS = BM_ / RPI;  // 1 KB loads that fill the A tile
+  static_assert(MB * 32 * WM == BM_ && NB * 32 * WN == BN, "tile geometry");
+  static_assert(NB % 2 == 0, "gate and up blocks pair up inside a wave");
+  static_assert(A_SLABS <= 4 * NLD && A_SLABS > 4 * (NLD - 1), "A tile loads");
+};
+
 // Weight row feeding row r (0..255) of N-tile tn.
-template <int EPI>
+template <int EPI, int NB>
 __device__ __forceinline__ int weight_row(const GemmArgs& g, int tn, int r) {
   if (EPI == EPI_IN) {
     const int n_qkv = 3 * g.D / BN;
     if (tn < n_qkv) return tn * BN + r;
-    // MLP tile: 128 hidden units; within a wave's 128 rows the 32-row groups
-    // alternate gate, up, gate, up
-    const int wn = r >> 7, grp = (r >> 5) & 3, i = r & 31;
-    const int hidden = (tn - n_qkv) * 128 + wn * 64 + (grp >> 1) * 32 + i;
-    return 3 * g.D + (grp & 1) * g.F + hidden;
+    // MLP tile: 128 hidden units.  Wave wn owns rows [32 NB wn, 32 NB (wn + 1));
+    // its 32-row blocks alternate gate, up, gate, up over the wave's NB / 2
+    // groups of 32 hidden units.
+    const int wn = r / (32 * NB), blk = (r >> 5) % NB, i = r & 31;
+    const int hidden = (tn - n_qkv) * 128 + wn * (NB / 2) * 32 + (blk >> 1) * 32 + i;
+    return 3 * g.D + (blk & 1) * g.F + hidden;
   }
   return tn * BN + r;
 }
@@ -97,8 +115,14 @@ __device__ __forceinline__ void ring_barrier() {
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
-template <int EPI>
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  return make_uint2(pack2(a, b), pack2(c, d));
+}
+
+template <int EPI, int BM>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
+  using T = Tile<BM>;
+  constexpr int MB = T::MB, NB = T::NB;
   // One LDS array per ring stage (A tile, then W tile), not one indexed array:
   // the compiler tracks direct-to-LDS stores per LDS variable, so it can see
   // that fragment reads of one stage never alias the loads in flight into the
@@ -114,7 +138,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   // wave index as a scalar: LDS addresses of the direct loads (M0) then come
   // from scalar arithmetic instead of a v_readfirstlane per load
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / T::WN, wn = wave % T::WN;
   const int ln = lane & 31, hl = lane >> 5;
 
   const int num_m = (g.M + BM - 1) / BM;
@@ -126,20 +150,25 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   const int tn = grp * GROUP_N + rem % gw;
 
   // Global -> LDS with gfx950's 16-byte direct loads (no staging registers).
-  // One wave instruction fills 1 KB of LDS = 16 tile rows of 64 B; lane i
-  // lands in row 16 j' + i / 4 at physical chunk i % 4, which holds logical
-  // chunk (i % 4) ^ swz(row) of the swizzled layout, so that is the chunk the
-  // lane fetches.  Wave w fills rows [64 w, 64 w + 64) of both tiles.
+  // One wave instruction fills 1 KB of LDS = 16 tile rows of 64 B (a slab);
+  // lane i lands in row 16 s + i / 4 at physical chunk i % 4, which holds
+  // logical chunk (i % 4) ^ swz(row), so that is the chunk the lane fetches.
+  // Wave w loads slabs 4 w .. 4 w + 3 of both tiles; when the A tile has
+  // fewer slabs (BM = 224) the last wave reloads its last slab, writing the
+  // same bytes to the same place, so every wave issues the same count.
   const int lrow = lane / CH;
   // byte offsets in 32 bits: the loads then use the scalar-base + vector-offset form
   uint32_t aoff[NLD], boff[NLD];
+  int aslab[NLD];
 #pragma unroll
   for (int j = 0; j < NLD; ++j) {
-    const int r = wave * (NLD * RPI) + RPI * j + lrow;
-    const int lch = (lane % CH) ^ swz(r);
-    const int arow = min(tm * BM + r, g.M - 1);
-    aoff[j] = ((uint32_t)arow * (uint32_t)g.K + lch * 8) * 2u;
-    boff[j] = ((uint32_t)weight_row<EPI>(g, tn, r) * (uint32_t)g.K + lch * 8) * 2u;
+    aslab[j] = min(wave * NLD + j, T::A_SLABS - 1);
+    const int ra = aslab[j] * RPI + lrow;
+    const int rb = (wave * NLD + j) * RPI + lrow;
+    const int arow = min(tm * BM + ra, g.M - 1);
+    aoff[j] = ((uint32_t)arow * (uint32_t)g.K + (((lane % CH) ^ swz(ra)) * 8)) * 2u;
+    boff[j] = ((uint32_t)weight_row<EPI, NB>(g, tn, rb) * (uint32_t)g.K +
+               (((lane % CH) ^ swz(rb)) * 8)) * 2u;
   }
   const char* abase = reinterpret_cast<const char*>(g.A);
   const char* bbase = reinterpret_cast<const char*>(g.W);
@@ -151,63 +180,63 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     const uint32_t ko = (uint32_t)min(kt, KT - 1) * (BK * 2);
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
-      const int slab = (wave * (NLD * RPI) + RPI * j) * BK;
-      __builtin_amdgcn_global_load_lds(abase + (aoff[j] + ko), (lds_ptr)(st + slab), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(bbase + (boff[j] + ko), (lds_ptr)(st + BM * BK + slab), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(abase + (aoff[j] + ko),
+                                       (lds_ptr)(st + aslab[j] * RPI * BK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bbase + (boff[j] + ko),
+                                       (lds_ptr)(st + BM * BK + (wave * NLD + j) * RPI * BK),
+                                       16, 0, 0);
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[MB][NB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // MFMA fragments, double-buffered in registers: while the 16 MFMAs of one
-  // 16-wide k step run, the 8 fragment reads of the next step are in flight.
-  bf16x8 fa[2][4], fb[2][4];
+  // MFMA fragments, double-buffered in registers: while the MFMAs of one
+  // 16-wide k step run, the fragment reads of the next step are in flight.
+  bf16x8 fa[2][MB], fb[2][NB];
   auto read_frags = [&](const uint16_t* st, int ks, int slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 128 + i * 32 + ln;
+    for (int i = 0; i < MB; ++i) {
+      const int r = (wm * MB + i) * 32 + ln;
       fa[slot][i] = *reinterpret_cast<const bf16x8*>(&st[r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wn * 128 + j * 32 + ln;
+    for (int j = 0; j < NB; ++j) {
+      const int r = (wn * NB + j) * 32 + ln;
       fb[slot][j] = *reinterpret_cast<const bf16x8*>(&st[BM * BK + r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
     }
   };
+  // C^T = W A^T: the weights are the A operand, so each lane ends up owning
+  // an output row (see the epilogue)
   auto mfmas = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0);
   };
   // One k tile from ring stage s.  The instruction order is pinned (the
   // compiler would otherwise sink the loads next to the waits and pair each
-  // fragment read with its first use).  The first k step interleaves its 16
-  // MFMAs with the 8 loads of the tile STAGES - 1 ahead and the 8 fragment
-  // reads of the second step.  The barrier then comes before the second k
-  // step, whose fragments are already in registers: the next tile's first
-  // fragment reads overlap those 16 MFMAs instead of stalling after the
-  // barrier.  That is safe because every read of stage s has completed before
-  // the barrier (lgkmcnt(0)), and stage s is refilled only after it.
+  // fragment read with its first use).  The first k step interleaves its
+  // MFMAs with the loads of the tile STAGES - 1 ahead and the fragment reads
+  // of the second step.  The barrier then comes before the second k step,
+  // whose fragments are already in registers: the next tile's first fragment
+  // reads overlap those MFMAs instead of stalling after the barrier.  That is
+  // safe because every read of stage s has completed before the barrier
+  // (lgkmcnt(0)), and stage s is refilled only after it.
   auto ktile = [&](int kt, int s) __attribute__((always_inline)) {
     gload(kt + STAGES - 1, ring[(s + STAGES - 1) % STAGES]);
     read_frags(ring[s], 1, 1);
     mfmas(0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MB * NB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global load
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -218,11 +247,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     read_frags(ring[(s + 1) % STAGES], 0, 0);
     mfmas(1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MB * NB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -237,25 +265,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  // Epilogue.  The MFMAs compute C^T (weights as the A operand), so in block
-  // (i, j) lane (ln, hl) holds output row i*32 + ln and the 4 consecutive
-  // columns j*32 + 8 rr + 4 hl .. + 3 in registers 4 rr .. 4 rr + 3: every
+  // Epilogue.  The MFMAs compute C^T, so in block (i, j) lane (ln, hl) holds
+  // output row (wm MB + i) 32 + ln and the 4 consecutive columns
+  // (wn NB + j) 32 + 8 rr + 4 hl .. + 3 in registers 4 rr .. 4 rr + 3: every
   // store, residual load and gate load is 8 contiguous bytes.
-  const int row_base = tm * BM + wm * 128;
-  const int col_base = tn * BN + wn * 128 + 4 * hl;
-  auto pack4 = [](float a, float b, float c, float d) __attribute__((always_inline)) {
-    return make_uint2(pack2(a, b), pack2(c, d));
-  };
+  const int row_base = tm * BM + wm * MB * 32 + ln;
+  const int col_base = tn * BN + wn * NB * 32 + 4 * hl;
   if (EPI == EPI_IN) {
     const int n_qkv = 3 * g.D / BN;
     if (tn < n_qkv) {
       // q | k | v: 4 consecutive columns never straddle a D boundary
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = row_base + i * 32 + ln;
+      for (int i = 0; i < MB; ++i) {
+        const int row = row_base + i * 32;
         if (row >= g.M) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int col = col_base + j * 32 + 8 * rr;
@@ -269,14 +294,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     } else {
       // SwiGLU: block 2p holds gate, block 2p + 1 up, of the same hidden units
       const int ldc = g.D + g.F;
-      const int hid_base = (tn - n_qkv) * 128 + wn * 64 + 4 * hl;
+      const int hid_base = (tn - n_qkv) * 128 + wn * (NB / 2) * 32 + 4 * hl;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = row_base + i * 32 + ln;
+      for (int i = 0; i < MB; ++i) {
+        const int row = row_base + i * 32;
         if (row >= g.M) continue;
         uint16_t* dst = g.cat + (size_t)row * ldc + g.D;
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
+        for (int p = 0; p < NB / 2; ++p)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const f32x16& ga = acc[i][2 * p];
@@ -291,18 +316,19 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   } else {
     const bool use_gate = !(g.flags & 2u), use_res = !(g.flags & 1u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = row_base + i * 32 + ln;
+    for (int i = 0; i < MB; ++i) {
+      const int row = row_base + i * 32;
       if (row >= g.M) continue;
       const uint16_t* gate = g.mod + (size_t)stream_of(row, g.e0, g.e1) * 3 * g.D + 2 * g.D;
       const uint16_t* xr = g.x + (size_t)row * g.D;
       uint16_t* yr = g.y + (size_t)row * g.D;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int col = col_base + j * 32 + 8 * rr;
-          const uint2 gv = use_gate ? *reinterpret_cast<const uint2*>(gate + col) : make_uint2(0x3f803f80u, 0x3f803f80u);
+          const uint2 gv = use_gate ? *reinterpret_cast<const uint2*>(gate + col)
+                                    : make_uint2(0x3f803f80u, 0x3f803f80u);
           const uint2 xv = use_res ? *reinterpret_cast<const uint2*>(xr + col) : make_uint2(0u, 0u);
           const f32x16& a = acc[i][j];
           *reinterpret_cast<uint2*>(yr + col) =
@@ -311,6 +337,45 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
         }
     }
   }
+}
+
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Tile height for M rows: fewest rounds of tiles over the CUs (one workgroup
+// per CU at a time), then the shorter tile.  The 224-row layout moves more
+// LDS data per MFMA than the 256-row one, so it only pays when it does not
+// add a round (4,256 tokens x 12 output tiles: 228 tiles in one round
+// instead of 204 taller ones).
+int pick_bm(int M, int num_n) {
+  const int cus = device_cus();
+  auto rounds = [&](int bm) {
+    const long tiles = (long)((M + bm - 1) / bm) * num_n;
+    return (tiles + cus - 1) / cus;
+  };
+  return rounds(224) <= rounds(256) ? 224 : 256;
+}
+
+template <int EPI>
+hipError_t launch(const GemmArgs& g, hipStream_t stream) {
+  const int bm = pick_bm(g.M, g.num_n);
+  const int tiles = ((g.M + bm - 1) / bm) * g.num_n;
+  if (bm == 224)
+    hipLaunchKernelGGL((gemm_kernel<EPI, 224>), dim3(tiles), dim3(256), 0, stream, g);
+  else
+    hipLaunchKernelGGL((gemm_kernel<EPI, 256>), dim3(tiles), dim3(256), 0, stream, g);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -330,9 +395,7 @@ hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D,
   g.k = k;
   g.v = v;
   g.cat = cat;
-  const int num_m = (M + BM - 1) / BM;
-  hipLaunchKernelGGL(gemm_kernel<EPI_IN>, dim3(num_m * g.num_n), dim3(256), 0, stream, g);
-  return hipGetLastError();
+  return launch<EPI_IN>(g, stream);
 }
 
 hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, int D, int F,
@@ -352,9 +415,7 @@ hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, in
   g.e0 = e0;
   g.e1 = e1;
   g.flags = flags;
-  const int num_m = (M + BM - 1) / BM;
-  hipLaunchKernelGGL(gemm_kernel<EPI_OUT>, dim3(num_m * g.num_n), dim3(256), 0, stream, g);
-  return hipGetLastError();
+  return launch<EPI_OUT>(g, stream);
 }
 
 }  // namespace dit

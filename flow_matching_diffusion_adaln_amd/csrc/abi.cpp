@@ -61,6 +61,7 @@ int check_desc(const dit_block_desc* d, Shape* sh) {
 
 struct Workspace {
   uint16_t *u, *q, *k, *v, *cat;
+  float* partial;  // GEMM split-K partial tiles
   size_t bytes;
 };
 
@@ -80,6 +81,8 @@ Workspace layout(const Shape& s, void* base) {
   off += round_up(nd);
   w.cat = reinterpret_cast<uint16_t*>(p + off);
   off += round_up(ncat);
+  w.partial = reinterpret_cast<float*>(p + off);
+  off += round_up(dit::kGemmPartialBytes);
   w.bytes = off;
   return w;
 }
@@ -125,7 +128,7 @@ int block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const 
     return rc;
   if ((rc = mark(DIT_STAGE_GEMM_IN))) return rc;
   if ((rc = hip_status(dit::launch_gemm_in(w.u, static_cast<const uint16_t*>(w_in), s.N, s.D,
-                                           s.F, w.q, w.k, w.v, w.cat, stream))))
+                                           s.F, w.q, w.k, w.v, w.cat, w.partial, stream))))
     return rc;
   if ((rc = mark(DIT_STAGE_ROPE))) return rc;
   if ((rc = hip_status(dit::launch_rope4(w.q, w.k, pos, static_cast<const uint16_t*>(q_scale),
@@ -139,7 +142,7 @@ int block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const 
   if ((rc = mark(DIT_STAGE_GEMM_OUT))) return rc;
   if ((rc = hip_status(dit::launch_gemm_out(w.cat, static_cast<const uint16_t*>(w_out), s.N,
                                             s.D, s.F, xb, mb, static_cast<uint16_t*>(y), s.e0,
-                                            s.e1, desc->flags, stream))))
+                                            s.e1, desc->flags, w.partial, stream))))
     return rc;
   return mark(DIT_N_STAGES);
 }

@@ -30,6 +30,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace dit {
 
 namespace {
@@ -40,6 +42,7 @@ constexpr int CH = BK / 8;           // 16-byte chunks per tile row (4)
 constexpr int RPI = 64 / CH;         // tile rows filled by one 1 KB wave load (16)
 constexpr int NLD = 4;               // loads per wave per k tile, for each of A and W
 constexpr int GROUP_N = 4;
+constexpr int kMaxPieces = GEMM_MAX_SPLIT_PIECES;  // split pieces per launch (kernels.h)
 
 enum { EPI_IN = 0, EPI_OUT = 1 };
 
@@ -59,6 +62,13 @@ struct GemmArgs {
   uint16_t* y;        // [M, D]
   int e0, e1;         // stream boundaries
   uint32_t flags;
+  // Split of the last, partial round of tiles (see launch()): tiles
+  // [0, n_dp) run whole, one per workgroup; the n_tail tiles after them are
+  // cut along K into n_pieces equal runs of 4-k-tile units, one per
+  // workgroup, whose fp32 partial tiles go to `partial` and are summed by the
+  // fix-up kernel.
+  int n_dp, n_tail, n_pieces;
+  float* partial;     // 2 * n_pieces slots of BM * BN floats
 };
 
 // Tile geometry: BM rows, WM x WN waves, MB x NB blocks of 32 x 32 per wave.
@@ -119,6 +129,100 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   return make_uint2(pack2(a, b), pack2(c, d));
 }
 
+// Logical tile id -> (tm, tn): groups of GROUP_N N-tiles, M fastest inside
+// a group, so the tiles one XCD runs together share few A and W panels.
+template <int BM>
+__device__ __forceinline__ void tile_coords(const GemmArgs& g, int id, int& tm, int& tn) {
+  const int num_m = (g.M + BM - 1) / BM;
+  const int grp = id / (GROUP_N * num_m);
+  const int rem = id - grp * GROUP_N * num_m;
+  const int gw = min(GROUP_N, g.num_n - grp * GROUP_N);
+  tm = rem / gw;
+  tn = grp * GROUP_N + rem % gw;
+}
+
+// Epilogue of one accumulator pair.  The MFMAs compute C^T, so in block
+// (i, j) of wave (wm, wn), lane (ln, hl) holds output row (wm MB + i) 32 + ln
+// and the 4 consecutive columns (wn NB + j) 32 + 8 rr + 4 hl .. + 3 in
+// registers 4 rr .. 4 rr + 3: every store, residual load and gate load is 8
+// contiguous bytes.  Blocks are taken in pairs j = 2 jp, 2 jp + 1 because the
+// SwiGLU tiles interleave them as (gate, up) of the same hidden units; `a` and
+// `b` are the two blocks' 4 values for one rr.
+template <int EPI, int BM>
+__device__ __forceinline__ void epilogue_pair(const GemmArgs& g, int tm, int tn, int wm, int wn,
+                                              int lane, int i, int jp, int rr, const float (&a)[4],
+                                              const float (&b)[4]) {
+  constexpr int MB = Tile<BM>::MB, NB = Tile<BM>::NB;
+  const int ln = lane & 31, hl = lane >> 5;
+  const int row = tm * BM + (wm * MB + i) * 32 + ln;
+  if (row >= g.M) return;
+  const int col = tn * BN + wn * NB * 32 + 4 * hl + 2 * jp * 32 + 8 * rr;  // block 2 jp
+  if (EPI == EPI_IN) {
+    const int n_qkv = 3 * g.D / BN;
+    if (tn < n_qkv) {
+      // q | k | v: D is a multiple of the 256-wide N tile, so the whole tile
+      // falls in one of the three
+      const int which = tn * BN / g.D;
+      uint16_t* const dr = (which == 0 ? g.q : which == 1 ? g.k : g.v) + (size_t)row * g.D +
+                           (col - which * g.D);
+      *reinterpret_cast<uint2*>(dr) = pack4(a[0], a[1], a[2], a[3]);
+      *reinterpret_cast<uint2*>(dr + 32) = pack4(b[0], b[1], b[2], b[3]);
+    } else {
+      const int hid = (tn - n_qkv) * 128 + wn * (NB / 2) * 32 + 4 * hl + jp * 32 + 8 * rr;
+      uint16_t* const dr = g.cat + (size_t)row * (g.D + g.F) + g.D + hid;
+      *reinterpret_cast<uint2*>(dr) = pack4(silu(a[0]) * b[0], silu(a[1]) * b[1],
+                                            silu(a[2]) * b[2], silu(a[3]) * b[3]);
+    }
+  } else {
+    const bool use_gate = !(g.flags & 2u), use_res = !(g.flags & 1u);
+    const uint16_t* gate = g.mod + (size_t)stream_of(row, g.e0, g.e1) * 3 * g.D + 2 * g.D + col;
+    const uint16_t* xr = g.x + (size_t)row * g.D + col;
+    uint16_t* yr = g.y + (size_t)row * g.D + col;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float(&v)[4] = h ? b : a;
+      const uint2 gv = use_gate ? *reinterpret_cast<const uint2*>(gate + 32 * h)
+                                : make_uint2(0x3f803f80u, 0x3f803f80u);
+      const uint2 xv = use_res ? *reinterpret_cast<const uint2*>(xr + 32 * h) : make_uint2(0u, 0u);
+      *reinterpret_cast<uint2*>(yr + 32 * h) =
+          pack4(fmaf(lo2f(gv.x), v[0], lo2f(xv.x)), fmaf(hi2f(gv.x), v[1], hi2f(xv.x)),
+                fmaf(lo2f(gv.y), v[2], lo2f(xv.y)), fmaf(hi2f(gv.y), v[3], hi2f(xv.y)));
+    }
+  }
+}
+
+template <int EPI, int BM>
+__device__ __forceinline__ void epilogue(const GemmArgs& g,
+                                         const f32x16 (&acc)[Tile<BM>::MB][Tile<BM>::NB], int tm,
+                                         int tn, int wm, int wn, int lane) {
+  constexpr int MB = Tile<BM>::MB, NB = Tile<BM>::NB;
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int jp = 0; jp < NB / 2; ++jp)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x16& x0 = acc[i][2 * jp];
+        const f32x16& x1 = acc[i][2 * jp + 1];
+        const float a[4] = {x0[4 * rr], x0[4 * rr + 1], x0[4 * rr + 2], x0[4 * rr + 3]};
+        const float b[4] = {x1[4 * rr], x1[4 * rr + 1], x1[4 * rr + 2], x1[4 * rr + 3]};
+        epilogue_pair<EPI, BM>(g, tm, tn, wm, wn, lane, i, jp, rr, a, b);
+      }
+}
+
+// A partial tile in fp32: wave w's accumulators as consecutive 16-byte
+// groups, group-major, so each wave store / load moves 1 KB contiguously.
+template <int BM>
+__device__ __forceinline__ float4* partial_slot(const GemmArgs& g, int slot, int wave, int lane) {
+  constexpr int G4 = Tile<BM>::MB * Tile<BM>::NB * 4;  // 16-byte groups per lane
+  return reinterpret_cast<float4*>(g.partial + (size_t)slot * BM * BN) + (size_t)wave * G4 * 64 + lane;
+}
+
+// First unit of piece p when `units` 4-k-tile units are cut into `pieces` runs.
+__device__ __forceinline__ int piece_start(int p, int units, int pieces) {
+  return (int)(((long long)p * units) / pieces);
+}
+
 template <int EPI, int BM>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   using T = Tile<BM>;
@@ -141,202 +245,222 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int ln = lane & 31, hl = lane >> 5;
 
-  const int num_m = (g.M + BM - 1) / BM;
-  const int id = xcd_remap(blockIdx.x, num_m * g.num_n);
-  const int grp = id / (GROUP_N * num_m);
-  const int rem = id - grp * GROUP_N * num_m;
-  const int gw = min(GROUP_N, g.num_n - grp * GROUP_N);
-  const int tm = rem / gw;
-  const int tn = grp * GROUP_N + rem % gw;
+  const int KT = g.K / BK;      // a multiple of STAGES for every supported shape
+  const int upt = KT / STAGES;  // 4-k-tile units per tile
 
-  // Global -> LDS with gfx950's 16-byte direct loads (no staging registers).
-  // One wave instruction fills 1 KB of LDS = 16 tile rows of 64 B (a slab);
-  // lane i lands in row 16 s + i / 4 at physical chunk i % 4, which holds
-  // logical chunk (i % 4) ^ swz(row), so that is the chunk the lane fetches.
-  // Wave w loads slabs 4 w .. 4 w + 3 of both tiles; when the A tile has
-  // fewer slabs (BM = 224) the last wave reloads its last slab, writing the
-  // same bytes to the same place, so every wave issues the same count.
-  const int lrow = lane / CH;
-  // byte offsets in 32 bits: the loads then use the scalar-base + vector-offset form
-  uint32_t aoff[NLD], boff[NLD];
-  int aslab[NLD];
-#pragma unroll
-  for (int j = 0; j < NLD; ++j) {
-    aslab[j] = min(wave * NLD + j, T::A_SLABS - 1);
-    const int ra = aslab[j] * RPI + lrow;
-    const int rb = (wave * NLD + j) * RPI + lrow;
-    const int arow = min(tm * BM + ra, g.M - 1);
-    aoff[j] = ((uint32_t)arow * (uint32_t)g.K + (((lane % CH) ^ swz(ra)) * 8)) * 2u;
-    boff[j] = ((uint32_t)weight_row<EPI, NB>(g, tn, rb) * (uint32_t)g.K +
-               (((lane % CH) ^ swz(rb)) * 8)) * 2u;
-  }
+  // Work items: one whole tile, or the one or two tail tiles a split piece
+  // covers (pieces are shorter than a tile).  Split piece p covers units [u0, u1) of the tail tiles, laid end to end.
+  const bool dp = (int)blockIdx.x < g.n_dp;
+  const int p = blockIdx.x - g.n_dp;
+  const int units = g.n_tail * upt;
+  const int u0 = dp ? 0 : piece_start(p, units, g.n_pieces);
+  const int u1 = dp ? 0 : piece_start(p + 1, units, g.n_pieces);
+  const int t0 = u0 / upt;
+  const int end0 = min(u1, (t0 + 1) * upt);
+
   const char* abase = reinterpret_cast<const char*>(g.A);
   const char* bbase = reinterpret_cast<const char*>(g.W);
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  const int KT = g.K / BK;  // a multiple of STAGES for every supported shape
-  // tile kt -> ring stage st; past the end the last tile is reloaded into the
-  // idle stage (never read), so the loop needs no branches
-  auto gload = [&](int kt, uint16_t* st) __attribute__((always_inline)) {
-    const uint32_t ko = (uint32_t)min(kt, KT - 1) * (BK * 2);
+  const int lrow = lane / CH;
+
+  // One work item: tile `id` over k tiles [k0, k1).  A whole tile (SPLIT
+  // false) ends in the epilogue, a split piece stores its fp32 partial tile in
+  // `slot`.  The two kinds are separate instances so neither carries the
+  // other's registers.
+  auto item = [&](auto split, int id, int k0, int k1, int slot) __attribute__((always_inline)) {
+    constexpr bool SPLIT = decltype(split)::value;
+    uint32_t aoff[NLD], boff[NLD];
+    int aslab[NLD];
+    f32x16 acc[MB][NB];
+    bf16x8 fa[2][MB], fb[2][NB];
+    int tm, tn;
+    tile_coords<BM>(g, id, tm, tn);
+
+    // Global -> LDS with gfx950's 16-byte direct loads (no staging registers).
+    // One wave instruction fills 1 KB of LDS = 16 tile rows of 64 B (a slab);
+    // lane i lands in row 16 s + i / 4 at physical chunk i % 4, which holds
+    // logical chunk (i % 4) ^ swz(row), so that is the chunk the lane fetches.
+    // Wave w loads slabs 4 w .. 4 w + 3 of both tiles; when the A tile has
+    // fewer slabs (BM = 224) the last wave reloads its last slab, writing the
+    // same bytes to the same place, so every wave issues the same count.
+    // Byte offsets are 32-bit: the loads use the scalar-base + vector-offset form.
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
-      __builtin_amdgcn_global_load_lds(abase + (aoff[j] + ko),
-                                       (lds_ptr)(st + aslab[j] * RPI * BK), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(bbase + (boff[j] + ko),
-                                       (lds_ptr)(st + BM * BK + (wave * NLD + j) * RPI * BK),
-                                       16, 0, 0);
+      aslab[j] = min(wave * NLD + j, T::A_SLABS - 1);
+      const int ra = aslab[j] * RPI + lrow;
+      const int rb = (wave * NLD + j) * RPI + lrow;
+      const int arow = min(tm * BM + ra, g.M - 1);
+      aoff[j] = ((uint32_t)arow * (uint32_t)g.K + (((lane % CH) ^ swz(ra)) * 8)) * 2u;
+      boff[j] = ((uint32_t)weight_row<EPI, NB>(g, tn, rb) * (uint32_t)g.K +
+                 (((lane % CH) ^ swz(rb)) * 8)) * 2u;
     }
-  };
+    // k tile kt -> ring stage (kt - k0) % STAGES; past k1 the last tile is
+    // reloaded into the idle stage (never read), so the loop needs no branches
+    auto gload = [&](int kt, uint16_t* st) __attribute__((always_inline)) {
+      const uint32_t ko = (uint32_t)min(kt, k1 - 1) * (BK * 2);
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        __builtin_amdgcn_global_load_lds(abase + (aoff[j] + ko),
+                                         (lds_ptr)(st + aslab[j] * RPI * BK), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(bbase + (boff[j] + ko),
+                                         (lds_ptr)(st + BM * BK + (wave * NLD + j) * RPI * BK),
+                                         16, 0, 0);
+      }
+    };
 
-  f32x16 acc[MB][NB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // MFMA fragments, double-buffered in registers: while the MFMAs of one
-  // 16-wide k step run, the fragment reads of the next step are in flight.
-  bf16x8 fa[2][MB], fb[2][NB];
-  auto read_frags = [&](const uint16_t* st, int ks, int slot) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int r = (wm * MB + i) * 32 + ln;
-      fa[slot][i] = *reinterpret_cast<const bf16x8*>(&st[r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int r = (wn * NB + j) * 32 + ln;
-      fb[slot][j] = *reinterpret_cast<const bf16x8*>(&st[BM * BK + r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
-    }
-  };
-  // C^T = W A^T: the weights are the A operand, so each lane ends up owning
-  // an output row (see the epilogue)
-  auto mfmas = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0);
-  };
-  // One k tile from ring stage s.  The instruction order is pinned (the
-  // compiler would otherwise sink the loads next to the waits and pair each
-  // fragment read with its first use).  The first k step interleaves its
-  // MFMAs with the loads of the tile STAGES - 1 ahead and the fragment reads
-  // of the second step.  The barrier then comes before the second k step,
-  // whose fragments are already in registers: the next tile's first fragment
-  // reads overlap those MFMAs instead of stalling after the barrier.  That is
-  // safe because every read of stage s has completed before the barrier
-  // (lgkmcnt(0)), and stage s is refilled only after it.
-  auto ktile = [&](int kt, int s) __attribute__((always_inline)) {
-    gload(kt + STAGES - 1, ring[(s + STAGES - 1) % STAGES]);
-    read_frags(ring[s], 1, 1);
-    mfmas(0);
 #pragma unroll
-    for (int i = 0; i < MB * NB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global load
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // tile kt + 1 must have landed; the STAGES - 2 younger tiles may still fly
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NLD * (STAGES - 2)));
-    __builtin_amdgcn_s_waitcnt(LGKMCNT0);
-    ring_barrier();
-    read_frags(ring[(s + 1) % STAGES], 0, 0);
-    mfmas(1);
-#pragma unroll
-    for (int i = 0; i < MB * NB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) gload(s, ring[s]);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NLD * (STAGES - 2)));
-  ring_barrier();
-  read_frags(ring[0], 0, 0);
-  for (int kt = 0; kt < KT; kt += STAGES) {
-#pragma unroll
-    for (int s = 0; s < STAGES; ++s) ktile(kt + s, s);
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-
-  // Epilogue.  The MFMAs compute C^T, so in block (i, j) lane (ln, hl) holds
-  // output row (wm MB + i) 32 + ln and the 4 consecutive columns
-  // (wn NB + j) 32 + 8 rr + 4 hl .. + 3 in registers 4 rr .. 4 rr + 3: every
-  // store, residual load and gate load is 8 contiguous bytes.
-  const int row_base = tm * BM + wm * MB * 32 + ln;
-  const int col_base = tn * BN + wn * NB * 32 + 4 * hl;
-  if (EPI == EPI_IN) {
-    const int n_qkv = 3 * g.D / BN;
-    if (tn < n_qkv) {
-      // q | k | v: 4 consecutive columns never straddle a D boundary
+    // MFMA fragments, double-buffered in registers: while the MFMAs of one
+    // 16-wide k step run, the fragment reads of the next step are in flight.
+    auto read_frags = [&](const uint16_t* st, int ks, int slot) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
-        const int row = row_base + i * 32;
-        if (row >= g.M) continue;
+        const int r = (wm * MB + i) * 32 + ln;
+        fa[slot][i] = *reinterpret_cast<const bf16x8*>(&st[r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int r = (wn * NB + j) * 32 + ln;
+        fb[slot][j] =
+            *reinterpret_cast<const bf16x8*>(&st[BM * BK + r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
+      }
+    };
+    // C^T = W A^T: the weights are the A operand, so each lane ends up owning
+    // an output row (see the epilogue)
+    auto mfmas = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0);
+    };
+    // One k tile from ring stage s.  The instruction order is pinned (the
+    // compiler would otherwise sink the loads next to the waits and pair each
+    // fragment read with its first use).  The first k step interleaves its
+    // MFMAs with the loads of the tile STAGES - 1 ahead and the fragment reads
+    // of the second step.  The barrier then comes before the second k step,
+    // whose fragments are already in registers: the next tile's first fragment
+    // reads overlap those MFMAs instead of stalling after the barrier.  That is
+    // safe because every read of stage s has completed before the barrier
+    // (lgkmcnt(0)), and stage s is refilled only after it.
+    auto ktile = [&](int kt, int s) __attribute__((always_inline)) {
+      gload(kt + STAGES - 1, ring[(s + STAGES - 1) % STAGES]);
+      read_frags(ring[s], 1, 1);
+      mfmas(0);
+#pragma unroll
+      for (int i = 0; i < MB * NB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global load
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // tile kt + 1 must have landed; the STAGES - 2 younger tiles may still fly
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NLD * (STAGES - 2)));
+      __builtin_amdgcn_s_waitcnt(LGKMCNT0);
+      ring_barrier();
+      read_frags(ring[(s + 1) % STAGES], 0, 0);
+      mfmas(1);
+#pragma unroll
+      for (int i = 0; i < MB * NB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) gload(k0 + s, ring[s]);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NLD * (STAGES - 2)));
+    ring_barrier();
+    read_frags(ring[0], 0, 0);
+    for (int kt = k0; kt < k1; kt += STAGES) {
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s) ktile(kt + s, s);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+    if constexpr (!SPLIT) {
+      epilogue<EPI, BM>(g, acc, tm, tn, wm, wn, lane);
+    } else {
+      float4* dst = partial_slot<BM>(g, slot, wave, lane);
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            const int col = col_base + j * 32 + 8 * rr;
-            const int which = col / g.D;
-            uint16_t* dst = which == 0 ? g.q : which == 1 ? g.k : g.v;
             const f32x16& a = acc[i][j];
-            *reinterpret_cast<uint2*>(dst + (size_t)row * g.D + (col - which * g.D)) =
-                pack4(a[4 * rr], a[4 * rr + 1], a[4 * rr + 2], a[4 * rr + 3]);
+            dst[((i * NB + j) * 4 + rr) * 64] =
+                make_float4(a[4 * rr], a[4 * rr + 1], a[4 * rr + 2], a[4 * rr + 3]);
           }
-      }
-    } else {
-      // SwiGLU: block 2p holds gate, block 2p + 1 up, of the same hidden units
-      const int ldc = g.D + g.F;
-      const int hid_base = (tn - n_qkv) * 128 + wn * (NB / 2) * 32 + 4 * hl;
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int row = row_base + i * 32;
-        if (row >= g.M) continue;
-        uint16_t* dst = g.cat + (size_t)row * ldc + g.D;
-#pragma unroll
-        for (int p = 0; p < NB / 2; ++p)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const f32x16& ga = acc[i][2 * p];
-            const f32x16& up = acc[i][2 * p + 1];
-            float m[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m[e] = silu(ga[4 * rr + e]) * up[4 * rr + e];
-            *reinterpret_cast<uint2*>(dst + hid_base + p * 32 + 8 * rr) = pack4(m[0], m[1], m[2], m[3]);
-          }
-      }
     }
+  };
+
+  if (dp) {
+    item(std::false_type{}, xcd_remap(blockIdx.x, g.n_dp), 0, KT, -1);
   } else {
-    const bool use_gate = !(g.flags & 2u), use_res = !(g.flags & 1u);
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int row = row_base + i * 32;
-      if (row >= g.M) continue;
-      const uint16_t* gate = g.mod + (size_t)stream_of(row, g.e0, g.e1) * 3 * g.D + 2 * g.D;
-      const uint16_t* xr = g.x + (size_t)row * g.D;
-      uint16_t* yr = g.y + (size_t)row * g.D;
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int col = col_base + j * 32 + 8 * rr;
-          const uint2 gv = use_gate ? *reinterpret_cast<const uint2*>(gate + col)
-                                    : make_uint2(0x3f803f80u, 0x3f803f80u);
-          const uint2 xv = use_res ? *reinterpret_cast<const uint2*>(xr + col) : make_uint2(0u, 0u);
-          const f32x16& a = acc[i][j];
-          *reinterpret_cast<uint2*>(yr + col) =
-              pack4(fmaf(lo2f(gv.x), a[4 * rr], lo2f(xv.x)), fmaf(hi2f(gv.x), a[4 * rr + 1], hi2f(xv.x)),
-                    fmaf(lo2f(gv.y), a[4 * rr + 2], lo2f(xv.y)), fmaf(hi2f(gv.y), a[4 * rr + 3], hi2f(xv.y)));
-        }
+    const int n_items = end0 < u1 ? 2 : 1;
+    for (int it = 0; it < n_items; ++it) {
+      // the ring is refilled for the next tile only after every wave is done
+      if (it) __syncthreads();
+      item(std::true_type{}, g.n_dp + t0 + it, it ? 0 : (u0 - t0 * upt) * STAGES,
+           it ? (u1 - (t0 + 1) * upt) * STAGES : (end0 - t0 * upt) * STAGES, 2 * p + it);
     }
   }
+}
+
+// Sums the partial tiles of the split tiles in K order (fixed, so results are
+// bitwise reproducible) and applies the epilogue.  One thread per pair of
+// 16-byte accumulator groups (blocks 2 jp and 2 jp + 1 of one wave, one rr,
+// one lane), so each wave load reads 1 KB contiguously and every thread has
+// two independent loads per partial in flight.
+template <int EPI, int BM>
+__global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
+  using T = Tile<BM>;
+  constexpr int MB = T::MB, NB = T::NB;
+  constexpr int PER_TILE = BM * BN / 8;  // threads per tile
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int t_rel = t / PER_TILE;
+  int rem = t - t_rel * PER_TILE;
+  const int lane = rem & 63;
+  rem >>= 6;
+  const int rr = rem & 3;
+  rem >>= 2;
+  const int jp = rem % (NB / 2);
+  rem /= NB / 2;
+  const int i = rem % MB;
+  const int wave = rem / MB;
+  const int wm = wave / T::WN, wn = wave % T::WN;
+  int tm, tn;
+  tile_coords<BM>(g, g.n_dp + t_rel, tm, tn);
+  const int upt = g.K / BK / STAGES;
+  const int units = g.n_tail * upt;
+  const int ua = t_rel * upt, ub = ua + upt;  // this tile's units
+  // first and last pieces that touch the tile
+  int pa = (int)(((long long)ua * g.n_pieces) / units);
+  while (pa > 0 && piece_start(pa, units, g.n_pieces) > ua) --pa;
+  while (piece_start(pa + 1, units, g.n_pieces) <= ua) ++pa;
+  int pb = pa;
+  while (pb + 1 < g.n_pieces && piece_start(pb + 1, units, g.n_pieces) < ub) ++pb;
+
+  const int g0 = ((i * NB + 2 * jp) * 4 + rr) * 64;  // group offsets in float4
+  const int g1 = g0 + 4 * 64;
+  float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int p = pa; p <= pb; ++p) {
+    // the tile is a piece's second item when the piece began in an earlier tile
+    const int slot = 2 * p + (piece_start(p, units, g.n_pieces) < ua ? 1 : 0);
+    const float4* src = partial_slot<BM>(g, slot, wave, lane);
+    const float4 va = src[g0], vb = src[g1];
+    a[0] += va.x; a[1] += va.y; a[2] += va.z; a[3] += va.w;
+    b[0] += vb.x; b[1] += vb.y; b[2] += vb.z; b[3] += vb.w;
+  }
+  epilogue_pair<EPI, BM>(g, tm, tn, wm, wn, lane, i, jp, rr, a, b);
 }
 
 // Compute units of the current device (queried once per device).
@@ -353,37 +477,85 @@ int device_cus() {
   return cached[dev];
 }
 
-// Tile height for M rows: fewest rounds of tiles over the CUs (one workgroup
-// per CU at a time), then the shorter tile.  The 224-row layout moves more
-// LDS data per MFMA than the 256-row one, so it only pays when it does not
-// add a round (4,256 tokens x 12 output tiles: 228 tiles in one round
-// instead of 204 taller ones).
-int pick_bm(int M, int num_n) {
+// Work plan of one GEMM launch.  With one workgroup per CU at a time, tiles
+// run in rounds of `cus`.  A last round holding only a few tiles would leave
+// most CUs idle for a whole tile time, so when at least one full round exists
+// and the last round is at most half full, its tail tiles are cut along K
+// into pieces of whole 4-k-tile units, one piece per CU (or per unit when
+// there are fewer units than CUs); the fix-up kernel then sums each tile's
+// fp32 partials in K order and runs the epilogue.
+struct Plan {
+  int bm, tiles, n_dp, n_tail, n_pieces;
+  float cost;  // estimated time in tile times
+};
+
+Plan make_plan(int bm, int M, int K, int num_n, bool can_split) {
   const int cus = device_cus();
-  auto rounds = [&](int bm) {
-    const long tiles = (long)((M + bm - 1) / bm) * num_n;
-    return (tiles + cus - 1) / cus;
-  };
-  return rounds(224) <= rounds(256) ? 224 : 256;
+  Plan p{};
+  p.bm = bm;
+  p.tiles = ((M + bm - 1) / bm) * num_n;
+  const int full = p.tiles / cus, tail = p.tiles - full * cus;
+  const int upt = K / BK / STAGES;
+  // a 224-row tile takes about as long as a 256-row one (the k loop's fixed
+  // per-step latency dominates), so cost is counted in tiles
+  const float tile_time = 1.0f;
+  if (can_split && full >= 1 && tail > 0 && 2 * tail <= cus) {
+    p.n_dp = full * cus;
+    p.n_tail = tail;
+    p.n_pieces = min(min(cus, kMaxPieces), tail * upt);
+    // the longest piece, plus partial stores and the fix-up pass
+    const int units = tail * upt;
+    const int longest = (units + p.n_pieces - 1) / p.n_pieces;
+    p.cost = tile_time * (full + (float)longest / upt + 0.1f);
+  } else {
+    p.n_dp = p.tiles;
+    p.n_tail = 0;
+    p.n_pieces = 0;
+    p.cost = tile_time * ((p.tiles + cus - 1) / cus);
+  }
+  return p;
+}
+
+// The 224-row layout (1 x 4 waves) gives a better round count for some M
+// (4,256 tokens x 12 output tiles: 228 tiles in one round, where 256-row tiles
+// need 204 but each is slower); the cheaper plan wins, ties going to the
+// shorter tile.
+Plan pick_plan(int M, int K, int num_n, bool can_split) {
+  const Plan a = make_plan(224, M, K, num_n, can_split);
+  const Plan b = make_plan(256, M, K, num_n, can_split);
+  return a.cost <= b.cost ? a : b;
 }
 
 template <int EPI>
-hipError_t launch(const GemmArgs& g, hipStream_t stream) {
-  const int bm = pick_bm(g.M, g.num_n);
-  const int tiles = ((g.M + bm - 1) / bm) * g.num_n;
+hipError_t launch(GemmArgs g, hipStream_t stream) {
+  const Plan p = pick_plan(g.M, g.K, g.num_n, g.partial != nullptr);
+  const int bm = p.bm;
+  g.n_dp = p.n_dp;
+  g.n_tail = p.n_tail;
+  g.n_pieces = p.n_pieces;
+  const int grid = g.n_dp + (g.n_tail ? g.n_pieces : 0);
   if (bm == 224)
-    hipLaunchKernelGGL((gemm_kernel<EPI, 224>), dim3(tiles), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((gemm_kernel<EPI, 224>), dim3(grid), dim3(256), 0, stream, g);
   else
-    hipLaunchKernelGGL((gemm_kernel<EPI, 256>), dim3(tiles), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((gemm_kernel<EPI, 256>), dim3(grid), dim3(256), 0, stream, g);
+  if (g.n_tail) {
+    if (bm == 224)
+      hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 224>), dim3(g.n_tail * 224 * BN / 8 / 256),
+                         dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 256>), dim3(g.n_tail * 256 * BN / 8 / 256),
+                         dim3(256), 0, stream, g);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D, int F,
-                          uint16_t* q, uint16_t* k, uint16_t* v, uint16_t* cat,
+                          uint16_t* q, uint16_t* k, uint16_t* v, uint16_t* cat, float* partial,
                           hipStream_t stream) {
   GemmArgs g{};
+  g.partial = partial;
   g.A = u;
   g.W = w_in;
   g.M = M;
@@ -400,8 +572,9 @@ hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D,
 
 hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, int D, int F,
                            const uint16_t* x, const uint16_t* mod, uint16_t* y, int e0, int e1,
-                           uint32_t flags, hipStream_t stream) {
+                           uint32_t flags, float* partial, hipStream_t stream) {
   GemmArgs g{};
+  g.partial = partial;
   g.A = cat;
   g.W = w_out;
   g.M = M;

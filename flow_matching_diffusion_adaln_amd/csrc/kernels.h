@@ -3,9 +3,15 @@
 #pragma once
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace dit {
+
+// Pieces a GEMM's tail round may be split into, and the fp32 scratch the
+// split needs (2 partial 256 x 256 tiles per piece).
+#define GEMM_MAX_SPLIT_PIECES 256
+constexpr size_t kGemmPartialBytes = (size_t)2 * GEMM_MAX_SPLIT_PIECES * 256 * 256 * 4;
 
 hipError_t launch_adaln(const uint16_t* x, const uint16_t* mod, uint16_t* out, int n_rows,
                         int width, int e0, int e1, float eps, hipStream_t stream);
@@ -19,11 +25,11 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        hipStream_t stream);
 
 hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D, int F,
-                          uint16_t* q, uint16_t* k, uint16_t* v, uint16_t* cat,
+                          uint16_t* q, uint16_t* k, uint16_t* v, uint16_t* cat, float* partial,
                           hipStream_t stream);
 
 hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, int D, int F,
                            const uint16_t* x, const uint16_t* mod, uint16_t* y, int e0, int e1,
-                           uint32_t flags, hipStream_t stream);
+                           uint32_t flags, float* partial, hipStream_t stream);
 
 }  // namespace dit

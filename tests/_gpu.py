@@ -46,15 +46,16 @@ def oracle_block(d, cfg, rows=None, flags=0):
 
 def sample_rows(cfg, n_random=48, seed=0):
     """Rows to check at full size: every stream's first and last rows, both
-    sides of each stream boundary, the last 256-row tile edge, and a random
-    spread."""
+    sides of each stream boundary, the last 224- and 256-row tile edges, and a
+    random spread."""
     N = cfg.N
     rows = {0, N - 1}
     e = 0
     for s in cfg.streams:
         rows.update({e, e + 1, e + s.n - 2, e + s.n - 1})
         e += s.n
-    rows.update({(N // 256) * 256 - 1, (N // 256) * 256})
+    for bm in (224, 256):  # the GEMMs' two row-tile heights
+        rows.update({(N // bm) * bm - 1, (N // bm) * bm})
     rng = np.random.default_rng(seed)
     rows.update(rng.choice(N, size=min(n_random, N), replace=False).tolist())
     return np.array(sorted(r for r in rows if 0 <= r < N))

@@ -159,6 +159,25 @@ def test_block_parity_single_token():
     check_block(block_config("one", (1,), 92))
 
 
+# On a 256-CU device these token counts make the GEMMs cut their last, partly
+# filled round of tiles along K (fp32 partial tiles + a fix-up pass):
+#   513:   input projection, 224-row tiles, 1 round + 68 tiles
+#   700:   input projection, 256-row tiles, 1 round + 68 tiles
+#   4,256: input projection, 256-row tiles, 7 rounds + 44 tiles (the 1024^2
+#          workload, covered by the c2 tests)
+#   5,601: both projections, 256-row tiles (output: 1 round + 8 tiles)
+#   6,000: both projections, 256-row tiles (output: 1 round + 32 tiles)
+@pytest.mark.parametrize("n_tokens,cid", [((449, 64), 93), ((620, 80), 94)])
+def test_block_parity_split_tail_small(n_tokens, cid):
+    check_block(block_config(f"split{sum(n_tokens)}", n_tokens, cid))
+
+
+@pytest.mark.parametrize("n_tokens,cid", [((5441, 160), 95), ((5840, 160), 96)])
+def test_block_parity_split_tail_both_gemms(n_tokens, cid):
+    cfg = block_config(f"split{sum(n_tokens)}", n_tokens, cid)
+    check_block(cfg, rows=sample_rows(cfg, n_random=32))
+
+
 def test_block_parity_c2_sampled():
     check_block(configs.C2, rows=sample_rows(configs.C2))
 

@@ -36,11 +36,10 @@ namespace dit {
 
 namespace {
 
-constexpr int BN = 256, BK = 32;
-constexpr int STAGES = 4;            // LDS ring depth; loads run STAGES - 1 tiles ahead
-constexpr int CH = BK / 8;           // 16-byte chunks per tile row (4)
-constexpr int RPI = 64 / CH;         // tile rows filled by one 1 KB wave load (16)
-constexpr int NLD = 4;               // loads per wave per k tile, for each of A and W
+constexpr int BN = 256, BK = 64;
+constexpr int STAGES = 2;            // LDS double buffer: a k tile loads while the previous one computes
+constexpr int CH = BK / 8;           // 16-byte chunks per tile row (8 = one 128-byte cache line)
+constexpr int RPI = 64 / CH;         // tile rows filled by one 1 KB wave load (8)
 constexpr int GROUP_N = 4;
 constexpr int kMaxPieces = GEMM_MAX_SPLIT_PIECES;  // split pieces per launch (kernels.h)
 
@@ -80,9 +79,11 @@ struct Tile {
   static constexpr int MB = BM_ / (32 * WM);
   static constexpr int NB = BN / (32 * WN);
   static constexpr int A_SLABS = BM_ / RPI;  // 1 KB loads that fill the A tile
+  static constexpr int NLD_A = A_SLABS / 4;  // per wave per k tile
+  static constexpr int NLD_B = BN / RPI / 4;
   static_assert(MB * 32 * WM == BM_ && NB * 32 * WN == BN, "tile geometry");
   static_assert(NB % 2 == 0, "gate and up blocks pair up inside a wave");
-  static_assert(A_SLABS <= 4 * NLD && A_SLABS > 4 * (NLD - 1), "A tile loads");
+  static_assert(NLD_A * 4 == A_SLABS, "A tile loads");
 };
 
 // Weight row feeding row r (0..255) of N-tile tn.
@@ -101,12 +102,12 @@ __device__ __forceinline__ int weight_row(const GemmArgs& g, int tn, int r) {
   return tn * BN + r;
 }
 
-// LDS tiles are rows of 32 bf16 (64 B = 4 chunks of 16 B).  gfx950's LDS has
-// 64 banks of 4 B, so 16 lanes of a 16-byte read are served per cycle: the
-// 16 consecutive rows one MFMA fragment read touches must land on 16
-// distinct 16-byte bank slots.  Row r covers slots 4 (r % 4) .. + 3, so the
-// chunk is xor-ed with (r >> 2) & 3, a bijection on the 4 rows of each class.
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+// LDS tiles are rows of 64 bf16 (128 B = 8 chunks of 16 B).  gfx950's LDS
+// has 64 banks of 4 B, so 16 lanes of a 16-byte read are served per cycle:
+// the 16 consecutive rows one MFMA fragment read touches must land on 16
+// distinct 16-byte bank slots.  Row r covers slots 8 (r % 2) .. + 7, so the
+// chunk is xor-ed with (r >> 1) & 7, a bijection on the 8 rows of each parity.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt left alone
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
@@ -234,9 +235,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   // A and W share one array per stage.)
   __shared__ __attribute__((aligned(16))) uint16_t s_st0[(BM + BN) * BK];
   __shared__ __attribute__((aligned(16))) uint16_t s_st1[(BM + BN) * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t s_st2[(BM + BN) * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t s_st3[(BM + BN) * BK];
-  uint16_t* const ring[STAGES] = {s_st0, s_st1, s_st2, s_st3};
+  uint16_t* const ring[STAGES] = {s_st0, s_st1};
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index as a scalar: LDS addresses of the direct loads (M0) then come
@@ -246,7 +245,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   const int ln = lane & 31, hl = lane >> 5;
 
   const int KT = g.K / BK;      // a multiple of STAGES for every supported shape
-  const int upt = KT / STAGES;  // 4-k-tile units per tile
+  const int upt = KT / STAGES;  // units (one k tile per ring stage) per tile
 
   // Work items: one whole tile, or the one or two tail tiles a split piece
   // covers (pieces are shorter than a tile).  Split piece p covers units [u0, u1) of the tail tiles, laid end to end.
@@ -269,28 +268,34 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   // other's registers.
   auto item = [&](auto split, int id, int k0, int k1, int slot) __attribute__((always_inline)) {
     constexpr bool SPLIT = decltype(split)::value;
-    uint32_t aoff[NLD], boff[NLD];
-    int aslab[NLD];
+    constexpr int NLD_A = T::NLD_A, NLD_B = T::NLD_B;
+    // fixed bounds (not NLD_A): an array of template-dependent type would make
+    // the direct-load builtins below dependent, and the host pass, which
+    // cannot check them, would then drop the kernel's host stub
+    uint32_t aoff[8], boff[8];
+    static_assert(NLD_A <= 8 && NLD_B <= 8, "load offsets");
     f32x16 acc[MB][NB];
     bf16x8 fa[2][MB], fb[2][NB];
     int tm, tn;
     tile_coords<BM>(g, id, tm, tn);
 
     // Global -> LDS with gfx950's 16-byte direct loads (no staging registers).
-    // One wave instruction fills 1 KB of LDS = 16 tile rows of 64 B (a slab);
-    // lane i lands in row 16 s + i / 4 at physical chunk i % 4, which holds
-    // logical chunk (i % 4) ^ swz(row), so that is the chunk the lane fetches.
-    // Wave w loads slabs 4 w .. 4 w + 3 of both tiles; when the A tile has
-    // fewer slabs (BM = 224) the last wave reloads its last slab, writing the
-    // same bytes to the same place, so every wave issues the same count.
-    // Byte offsets are 32-bit: the loads use the scalar-base + vector-offset form.
+    // One wave instruction fills 1 KB of LDS = 8 tile rows of 128 B (a slab),
+    // so it reads 8 whole cache lines: the vector L1 delivers twice the bytes
+    // per cycle that it does for half lines.  Lane i lands in row 8 s + i / 8
+    // at physical chunk i % 8, which holds logical chunk (i % 8) ^ swz(row), so
+    // that is the chunk the lane fetches.  Wave w loads A slabs
+    // NLD_A w .. NLD_A (w + 1) - 1 and W slabs likewise.  Byte offsets are
+    // 32-bit: the loads use the scalar-base + vector-offset form.
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      aslab[j] = min(wave * NLD + j, T::A_SLABS - 1);
-      const int ra = aslab[j] * RPI + lrow;
-      const int rb = (wave * NLD + j) * RPI + lrow;
+    for (int j = 0; j < NLD_A; ++j) {
+      const int ra = (wave * NLD_A + j) * RPI + lrow;
       const int arow = min(tm * BM + ra, g.M - 1);
       aoff[j] = ((uint32_t)arow * (uint32_t)g.K + (((lane % CH) ^ swz(ra)) * 8)) * 2u;
+    }
+#pragma unroll
+    for (int j = 0; j < NLD_B; ++j) {
+      const int rb = (wave * NLD_B + j) * RPI + lrow;
       boff[j] = ((uint32_t)weight_row<EPI, NB>(g, tn, rb) * (uint32_t)g.K +
                  (((lane % CH) ^ swz(rb)) * 8)) * 2u;
     }
@@ -299,13 +304,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     auto gload = [&](int kt, uint16_t* st) __attribute__((always_inline)) {
       const uint32_t ko = (uint32_t)min(kt, k1 - 1) * (BK * 2);
 #pragma unroll
-      for (int j = 0; j < NLD; ++j) {
+      for (int j = 0; j < NLD_A; ++j)
         __builtin_amdgcn_global_load_lds(abase + (aoff[j] + ko),
-                                         (lds_ptr)(st + aslab[j] * RPI * BK), 16, 0, 0);
+                                         (lds_ptr)(st + (wave * NLD_A + j) * RPI * BK), 16, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NLD_B; ++j)
         __builtin_amdgcn_global_load_lds(bbase + (boff[j] + ko),
-                                         (lds_ptr)(st + BM * BK + (wave * NLD + j) * RPI * BK),
+                                         (lds_ptr)(st + BM * BK + (wave * NLD_B + j) * RPI * BK),
                                          16, 0, 0);
-      }
     };
 
 #pragma unroll
@@ -340,19 +346,34 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
           acc[i][j] =
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0);
     };
-    // One k tile from ring stage s.  The instruction order is pinned (the
-    // compiler would otherwise sink the loads next to the waits and pair each
-    // fragment read with its first use).  The first k step interleaves its
-    // MFMAs with the loads of the tile STAGES - 1 ahead and the fragment reads
-    // of the second step.  The barrier then comes before the second k step,
-    // whose fragments are already in registers: the next tile's first fragment
-    // reads overlap those MFMAs instead of stalling after the barrier.  That is
-    // safe because every read of stage s has completed before the barrier
-    // (lgkmcnt(0)), and stage s is refilled only after it.
+    // One k tile (4 k steps of 16) from ring stage s, while tile kt + 1 lands
+    // in the other stage.  The instruction order is pinned (the compiler would
+    // otherwise sink the loads next to the waits and pair each fragment read
+    // with its first use).  Each k step's MFMAs run while the next step's
+    // fragment reads are in flight.  The barrier comes before the last k
+    // step, whose fragments are already in registers: every read of stage s
+    // is then complete (lgkmcnt(0)), so right after the barrier stage s is
+    // refilled with tile kt + 2 and the first fragments of tile kt + 1 are
+    // read, both overlapping the last k step's MFMAs.
     auto ktile = [&](int kt, int s) __attribute__((always_inline)) {
-      gload(kt + STAGES - 1, ring[(s + STAGES - 1) % STAGES]);
-      read_frags(ring[s], 1, 1);
-      mfmas(0);
+#pragma unroll
+      for (int ks = 0; ks < 3; ++ks) {
+        read_frags(ring[s], ks + 1, (ks + 1) & 1);
+        mfmas(ks & 1);
+#pragma unroll
+        for (int i = 0; i < MB * NB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // tile kt + 1 has landed (it is the only one in flight)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __builtin_amdgcn_s_waitcnt(LGKMCNT0);
+      ring_barrier();
+      gload(kt + 2, ring[s]);
+      read_frags(ring[s ^ 1], 0, 0);
+      mfmas(1);
 #pragma unroll
       for (int i = 0; i < MB * NB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
@@ -360,28 +381,16 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
       }
       __builtin_amdgcn_sched_barrier(0);
-      // tile kt + 1 must have landed; the STAGES - 2 younger tiles may still fly
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NLD * (STAGES - 2)));
-      __builtin_amdgcn_s_waitcnt(LGKMCNT0);
-      ring_barrier();
-      read_frags(ring[(s + 1) % STAGES], 0, 0);
-      mfmas(1);
-#pragma unroll
-      for (int i = 0; i < MB * NB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
     };
 
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) gload(k0 + s, ring[s]);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NLD * (STAGES - 2)));
+    gload(k0, ring[0]);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     ring_barrier();
+    gload(k0 + 1, ring[1]);
     read_frags(ring[0], 0, 0);
     for (int kt = k0; kt < k1; kt += STAGES) {
-#pragma unroll
-      for (int s = 0; s < STAGES; ++s) ktile(kt + s, s);
+      ktile(kt, 0);
+      ktile(kt + 1, 1);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 

@@ -37,7 +37,7 @@ namespace dit {
 namespace {
 
 constexpr int BN = 256, BK = 64;
-constexpr int STAGES = 2;            // LDS double buffer: a k tile loads while the previous one computes
+constexpr int NW = 2;                // LDS slots for W k tiles (double buffer)
 constexpr int CH = BK / 8;           // 16-byte chunks per tile row (8 = one 128-byte cache line)
 constexpr int RPI = 64 / CH;         // tile rows filled by one 1 KB wave load (8)
 constexpr int GROUP_N = 4;
@@ -63,10 +63,11 @@ struct GemmArgs {
   uint32_t flags;
   // Split of the last, partial round of tiles (see launch()): tiles
   // [0, n_dp) run whole, one per workgroup; the n_tail tiles after them are
-  // cut along K into n_pieces equal runs of 4-k-tile units, one per
+  // cut along K into n_pieces equal runs of whole units, one per
   // workgroup, whose fp32 partial tiles go to `partial` and are summed by the
   // fix-up kernel.
   int n_dp, n_tail, n_pieces;
+  int unit;           // k tiles per split unit (the K loop's unroll period)
   float* partial;     // 2 * n_pieces slots of BM * BN floats
 };
 
@@ -224,18 +225,28 @@ __device__ __forceinline__ int piece_start(int p, int units, int pieces) {
   return (int)(((long long)p * units) / pieces);
 }
 
-template <int EPI, int BM>
+// NA: LDS slots for A k tiles.  NA = 3 lets the A loads of tile kt + 2 start
+// during the first k steps of tile kt (A is the operand that misses L2 more:
+// each A panel is shared by fewer concurrent tiles than a W panel), spread
+// over them instead of bursting after the barrier; the K loop's unroll period
+// is then lcm(3, 2) = 6 k tiles.  NA = 2 serves K that is not a multiple of
+// 6 k tiles; then both operands load right after the barrier.
+template <int EPI, int BM, int NA>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   using T = Tile<BM>;
   constexpr int MB = T::MB, NB = T::NB;
-  // One LDS array per ring stage (A tile, then W tile), not one indexed array:
-  // the compiler tracks direct-to-LDS stores per LDS variable, so it can see
-  // that fragment reads of one stage never alias the loads in flight into the
-  // others and does not wait on them.  (It tracks only a few variables, hence
-  // A and W share one array per stage.)
-  __shared__ __attribute__((aligned(16))) uint16_t s_st0[(BM + BN) * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t s_st1[(BM + BN) * BK];
-  uint16_t* const ring[STAGES] = {s_st0, s_st1};
+  constexpr int PERIOD = NA == 3 ? 6 : 2;
+  // One LDS array per slot, not one indexed array: the compiler tracks
+  // direct-to-LDS stores per LDS variable, so it can see that fragment reads
+  // of one slot never alias the loads in flight into the others and does not
+  // wait on them.  NA = 3 and BM = 256 use all 160 KB.
+  __shared__ __attribute__((aligned(16))) uint16_t s_a0[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a1[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a2[NA == 3 ? BM * BK : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w0[BN * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w1[BN * BK];
+  uint16_t* const ring_a[3] = {s_a0, s_a1, s_a2};
+  uint16_t* const ring_w[NW] = {s_w0, s_w1};
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index as a scalar: LDS addresses of the direct loads (M0) then come
@@ -244,8 +255,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int ln = lane & 31, hl = lane >> 5;
 
-  const int KT = g.K / BK;      // a multiple of STAGES for every supported shape
-  const int upt = KT / STAGES;  // units (one k tile per ring stage) per tile
+  const int KT = g.K / BK;      // a multiple of PERIOD (the host picks NA so)
+  const int upt = KT / PERIOD;  // split units per tile
 
   // Work items: one whole tile, or the one or two tail tiles a split piece
   // covers (pieces are shorter than a tile).  Split piece p covers units [u0, u1) of the tail tiles, laid end to end.
@@ -299,19 +310,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
       boff[j] = ((uint32_t)weight_row<EPI, NB>(g, tn, rb) * (uint32_t)g.K +
                  (((lane % CH) ^ swz(rb)) * 8)) * 2u;
     }
-    // k tile kt -> ring stage (kt - k0) % STAGES; past k1 the last tile is
-    // reloaded into the idle stage (never read), so the loop needs no branches
-    auto gload = [&](int kt, uint16_t* st) __attribute__((always_inline)) {
+    // Past k1 the last tile is reloaded into an idle slot (never read), so
+    // the loop needs no branches.  gload_a issues A loads j0 .. j1 - 1 of k
+    // tile kt, so they can be spread over several k steps.
+    auto gload_a = [&](int kt, uint16_t* st, int j0, int j1) __attribute__((always_inline)) {
       const uint32_t ko = (uint32_t)min(kt, k1 - 1) * (BK * 2);
 #pragma unroll
-      for (int j = 0; j < NLD_A; ++j)
+      for (int j = j0; j < j1; ++j)
         __builtin_amdgcn_global_load_lds(abase + (aoff[j] + ko),
                                          (lds_ptr)(st + (wave * NLD_A + j) * RPI * BK), 16, 0, 0);
+    };
+    auto gload_w = [&](int kt, uint16_t* st) __attribute__((always_inline)) {
+      const uint32_t ko = (uint32_t)min(kt, k1 - 1) * (BK * 2);
 #pragma unroll
       for (int j = 0; j < NLD_B; ++j)
         __builtin_amdgcn_global_load_lds(bbase + (boff[j] + ko),
-                                         (lds_ptr)(st + BM * BK + (wave * NLD_B + j) * RPI * BK),
-                                         16, 0, 0);
+                                         (lds_ptr)(st + (wave * NLD_B + j) * RPI * BK), 16, 0, 0);
     };
 
 #pragma unroll
@@ -323,17 +337,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 
     // MFMA fragments, double-buffered in registers: while the MFMAs of one
     // 16-wide k step run, the fragment reads of the next step are in flight.
-    auto read_frags = [&](const uint16_t* st, int ks, int slot) __attribute__((always_inline)) {
+    auto read_frags = [&](const uint16_t* sa, const uint16_t* sw, int ks, int slot)
+                          __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         const int r = (wm * MB + i) * 32 + ln;
-        fa[slot][i] = *reinterpret_cast<const bf16x8*>(&st[r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
+        fa[slot][i] = *reinterpret_cast<const bf16x8*>(&sa[r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int r = (wn * NB + j) * 32 + ln;
-        fb[slot][j] =
-            *reinterpret_cast<const bf16x8*>(&st[BM * BK + r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
+        fb[slot][j] = *reinterpret_cast<const bf16x8*>(&sw[r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
       }
     };
     // C^T = W A^T: the weights are the A operand, so each lane ends up owning
@@ -346,36 +360,48 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
           acc[i][j] =
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0);
     };
-    // One k tile (4 k steps of 16) from ring stage s, while tile kt + 1 lands
-    // in the other stage.  The instruction order is pinned (the compiler would
-    // otherwise sink the loads next to the waits and pair each fragment read
-    // with its first use).  Each k step's MFMAs run while the next step's
-    // fragment reads are in flight.  The barrier comes before the last k
-    // step, whose fragments are already in registers: every read of stage s
-    // is then complete (lgkmcnt(0)), so right after the barrier stage s is
-    // refilled with tile kt + 2 and the first fragments of tile kt + 1 are
-    // read, both overlapping the last k step's MFMAs.
-    auto ktile = [&](int kt, int s) __attribute__((always_inline)) {
+    // One k tile (4 k steps of 16) from A slot i % NA and W slot i % 2, while
+    // tile kt + 1 lands in the other slots.  The instruction order is pinned
+    // (the compiler would otherwise sink the loads next to the waits and pair
+    // each fragment read with its first use).  Each k step's MFMAs run while
+    // the next step's fragment reads are in flight.  With NA = 3 the A loads
+    // of tile kt + 2 go to the slot tile kt - 1 used, free since the previous
+    // barrier, and are spread over k steps 0..2.  The barrier comes before the
+    // last k step, whose fragments are already in registers: every read of
+    // this tile's slots is then complete (lgkmcnt(0)), so right after the
+    // barrier the W slot (and with NA = 2 the A slot) is refilled with tile
+    // kt + 2 and the first fragments of tile kt + 1 are read, all overlapping
+    // the last k step's MFMAs.
+    auto ktile = [&](int kt, int i) __attribute__((always_inline)) {
+      uint16_t* const sa = ring_a[i % NA];
+      uint16_t* const sw = ring_w[i % NW];
 #pragma unroll
       for (int ks = 0; ks < 3; ++ks) {
-        read_frags(ring[s], ks + 1, (ks + 1) & 1);
+        if constexpr (NA == 3) {
+          // A loads of tile kt + 2: NLD_A split as evenly as possible
+          gload_a(kt + 2, ring_a[(i + 2) % 3], ks * NLD_A / 3, (ks + 1) * NLD_A / 3);
+        }
+        read_frags(sa, sw, ks + 1, (ks + 1) & 1);
         mfmas(ks & 1);
 #pragma unroll
-        for (int i = 0; i < MB * NB; ++i) {
+        for (int q = 0; q < MB * NB; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+          if (NA == 3 && (q & 3) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // tile kt + 1 has landed (it is the only one in flight)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      // tile kt + 1 has landed; with NA = 3 the A loads of tile kt + 2 (the
+      // youngest NLD_A) may still fly
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NA == 3 ? NLD_A : 0));
       __builtin_amdgcn_s_waitcnt(LGKMCNT0);
       ring_barrier();
-      gload(kt + 2, ring[s]);
-      read_frags(ring[s ^ 1], 0, 0);
+      if constexpr (NA == 2) gload_a(kt + 2, sa, 0, NLD_A);
+      gload_w(kt + 2, sw);
+      read_frags(ring_a[(i + 1) % NA], ring_w[(i + 1) % NW], 0, 0);
       mfmas(1);
 #pragma unroll
-      for (int i = 0; i < MB * NB; ++i) {
+      for (int q = 0; q < MB * NB; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global load
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
@@ -383,14 +409,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    gload(k0, ring[0]);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // prologue: tiles k0 and k0 + 1 in flight, wait for k0
+    gload_a(k0, ring_a[0], 0, NLD_A);
+    gload_w(k0, ring_w[0]);
+    gload_a(k0 + 1, ring_a[1], 0, NLD_A);
+    gload_w(k0 + 1, ring_w[1]);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NLD_A + NLD_B));
     ring_barrier();
-    gload(k0 + 1, ring[1]);
-    read_frags(ring[0], 0, 0);
-    for (int kt = k0; kt < k1; kt += STAGES) {
-      ktile(kt, 0);
-      ktile(kt + 1, 1);
+    read_frags(ring_a[0], ring_w[0], 0, 0);
+    for (int kt = k0; kt < k1; kt += PERIOD) {
+#pragma unroll
+      for (int i = 0; i < PERIOD; ++i) ktile(kt + i, i);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
@@ -418,8 +447,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     for (int it = 0; it < n_items; ++it) {
       // the ring is refilled for the next tile only after every wave is done
       if (it) __syncthreads();
-      item(std::true_type{}, g.n_dp + t0 + it, it ? 0 : (u0 - t0 * upt) * STAGES,
-           it ? (u1 - (t0 + 1) * upt) * STAGES : (end0 - t0 * upt) * STAGES, 2 * p + it);
+      item(std::true_type{}, g.n_dp + t0 + it, it ? 0 : (u0 - t0 * upt) * PERIOD,
+           it ? (u1 - (t0 + 1) * upt) * PERIOD : (end0 - t0 * upt) * PERIOD, 2 * p + it);
     }
   }
 }
@@ -448,7 +477,7 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
   const int wm = wave / T::WN, wn = wave % T::WN;
   int tm, tn;
   tile_coords<BM>(g, g.n_dp + t_rel, tm, tn);
-  const int upt = g.K / BK / STAGES;
+  const int upt = g.K / BK / g.unit;
   const int units = g.n_tail * upt;
   const int ua = t_rel * upt, ub = ua + upt;  // this tile's units
   // first and last pieces that touch the tile
@@ -493,6 +522,10 @@ int device_cus() {
 // into pieces of whole 4-k-tile units, one piece per CU (or per unit when
 // there are fewer units than CUs); the fix-up kernel then sums each tile's
 // fp32 partials in K order and runs the epilogue.
+// K loop unroll period in k tiles: 6 (3 A slots) when it divides K / BK,
+// else 2 (K is a multiple of 128 for every supported shape).
+int unroll_period(int K) { return (K / BK) % 6 == 0 ? 6 : 2; }
+
 struct Plan {
   int bm, tiles, n_dp, n_tail, n_pieces;
   float cost;  // estimated time in tile times
@@ -504,7 +537,7 @@ Plan make_plan(int bm, int M, int K, int num_n, bool can_split) {
   p.bm = bm;
   p.tiles = ((M + bm - 1) / bm) * num_n;
   const int full = p.tiles / cus, tail = p.tiles - full * cus;
-  const int upt = K / BK / STAGES;
+  const int upt = K / BK / unroll_period(K);
   // a 224-row tile takes about as long as a 256-row one (the k loop's fixed
   // per-step latency dominates), so cost is counted in tiles
   const float tile_time = 1.0f;
@@ -542,11 +575,19 @@ hipError_t launch(GemmArgs g, hipStream_t stream) {
   g.n_dp = p.n_dp;
   g.n_tail = p.n_tail;
   g.n_pieces = p.n_pieces;
+  g.unit = unroll_period(g.K);
   const int grid = g.n_dp + (g.n_tail ? g.n_pieces : 0);
-  if (bm == 224)
-    hipLaunchKernelGGL((gemm_kernel<EPI, 224>), dim3(grid), dim3(256), 0, stream, g);
-  else
-    hipLaunchKernelGGL((gemm_kernel<EPI, 256>), dim3(grid), dim3(256), 0, stream, g);
+  if (g.unit == 6) {
+    if (bm == 224)
+      hipLaunchKernelGGL((gemm_kernel<EPI, 224, 3>), dim3(grid), dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((gemm_kernel<EPI, 256, 3>), dim3(grid), dim3(256), 0, stream, g);
+  } else {
+    if (bm == 224)
+      hipLaunchKernelGGL((gemm_kernel<EPI, 224, 2>), dim3(grid), dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((gemm_kernel<EPI, 256, 2>), dim3(grid), dim3(256), 0, stream, g);
+  }
   if (g.n_tail) {
     if (bm == 224)
       hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 224>), dim3(g.n_tail * 224 * BN / 8 / 256),

@@ -61,8 +61,9 @@ def sample_rows(cfg, n_random=48, seed=0):
     return np.array(sorted(r for r in rows if 0 <= r < N))
 
 
-def block_config(name, n_tokens, config_id):
-    """A joint-block config with the given token counts (image | [reference] | text)."""
+def block_config(name, n_tokens, config_id, **dims):
+    """A joint-block config with the given token counts (image | [reference] | text);
+    `dims` may override width, n_heads, head_dim and mlp_hidden."""
     kinds = {1: ("image",), 2: ("image", "text"), 3: ("image", "reference", "text")}[len(n_tokens)]
     streams = []
     for kind, n in zip(kinds, n_tokens):
@@ -70,4 +71,4 @@ def block_config(name, n_tokens, config_id):
             streams.append(configs.Stream("text", n))
         else:
             streams.append(configs.Stream(kind, n, (1, n), 0.0 if kind == "reference" else 0.7))
-    return configs.BlockConfig(name, config_id, tuple(streams))
+    return configs.BlockConfig(name, config_id, tuple(streams), **dims)

@@ -178,6 +178,13 @@ def test_block_parity_split_tail_both_gemms(n_tokens, cid):
     check_block(cfg, rows=sample_rows(cfg, n_random=32))
 
 
+def test_block_parity_narrow_width():
+    # width 2,048 (16 heads), SwiGLU 6,144: K = 2,048 and 8,192 are not
+    # multiples of 6 k tiles of 64, so both GEMMs run their 2-slot A ring
+    cfg = block_config("w2048", (700, 80), 97, width=2048, n_heads=16, mlp_hidden=6144)
+    check_block(cfg, rows=sample_rows(cfg, n_random=32))
+
+
 def test_block_parity_c2_sampled():
     check_block(configs.C2, rows=sample_rows(configs.C2))
 

@@ -6,10 +6,12 @@
 // (the DiT takes no padding mask).  No mask is applied.
 //
 // Design (gfx950, 64-wide waves, 32x32x16 bf16 MFMA, 64-bank LDS):
-//  * A workgroup is one head x 128 queries; each of its 4 waves owns 32
-//    queries for the whole key loop.  Keys stream through LDS in tiles of 64,
-//    double-buffered; K and V go from HBM/L2 straight into LDS with the
-//    16-byte direct-to-LDS loads, no staging registers.
+//  * A workgroup is one head x 256 queries; each of its 8 waves owns 32
+//    queries for the whole key loop.  Keys stream through LDS in tiles of 64;
+//    K and V go from HBM/L2 straight into LDS with the 16-byte direct-to-LDS
+//    loads, no staging registers.  Bringing K and V into a CU is the costly
+//    part (more than the exp of the softmax), so a workgroup serves as many
+//    queries as 2 waves per SIMD allow: one K/V tile feeds 256 queries.
 //  * Scores are computed transposed, S^T = K Q^T (A = K from LDS, B = Q held
 //    in registers).  In the 32x32 MFMA result a lane holds one column, so
 //    each lane owns one query: row max and row sum are in-lane reductions
@@ -33,12 +35,16 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace dit {
 
 namespace {
 
-constexpr int BQ = 128;   // queries per workgroup
+constexpr int NWAVE = 8;  // waves per workgroup (32 queries each)
+constexpr int BQ = 32 * NWAVE;  // queries per workgroup
 constexpr int BKEY = 64;  // keys per tile
+constexpr int LPW = BKEY / 4 / NWAVE;  // 1 KB loads per wave per K (or V) tile
 constexpr int HD = 128;   // head dim
 constexpr float RESCALE_LOG2 = 8.f;
 
@@ -67,11 +73,24 @@ __device__ __forceinline__ int key_slot(int m) {
   return 16 * (r >> 1) + 8 * h + 4 * (r & 1) + j;
 }
 
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt immediates: vmcnt(4) / vmcnt(0), expcnt and lgkmcnt left alone
+constexpr int vmcnt_imm_lpw() { return LPW | 0x0F70; }
+constexpr int vmcnt_imm0() { return 0x0F70; }
+
+// Workgroup barrier that does not wait for outstanding vector-memory loads
+// (__syncthreads() waits for all of them, the whole prefetch ring); LDS
+// reads are completed first so a slot can be refilled after it.  The empty
+// asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_keep_loads() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v,
                                                           uint16_t* __restrict__ o, int N,
@@ -102,26 +121,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 
   // Direct-to-LDS loads: a wave instruction fills 1 KB = 4 rows of 256 B;
   // lane i lands in row 4 j' + i / 16 at physical chunk i % 16.  Wave w
-  // fills rows [16 w, 16 w + 16) of both tiles.
+  // fills rows [4 LPW w, 4 LPW (w + 1)) of a tile.
   const char* kbase = reinterpret_cast<const char*>(k + (size_t)h * HD);
   const char* vbase = reinterpret_cast<const char*>(v + (size_t)h * HD);
   const int prow = lane >> 4, pch = lane & 15;
-  uint32_t kch[4], vch[4];  // byte offset of the chunk this lane fetches, per slab
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = wave * 16 + 4 * j + prow;
-    kch[j] = (uint32_t)((pch ^ kswz(r)) * 16);
-    vch[j] = (uint32_t)(((((pch >> 2) ^ vswz(r)) << 2) | (pch & 3)) * 16);
-  }
+  // byte offsets of the chunk this lane fetches for slab j (recomputed per
+  // load: a few integer ops instead of 8 live registers)
+  auto kch = [&](int j) __attribute__((always_inline)) {
+    return (uint32_t)((pch ^ kswz(wave * 4 * LPW + 4 * j + prow)) * 16);
+  };
+  auto vch = [&](int j) __attribute__((always_inline)) {
+    return (uint32_t)(((((pch >> 2) ^ vswz(wave * 4 * LPW + 4 * j + prow)) << 2) | (pch & 3)) * 16);
+  };
   const uint32_t row_bytes = (uint32_t)ld_qkv * 2u;
-  auto dma = [&](int t, uint16_t* sk, uint16_t* sv) {
+  const int ntiles = (N + BKEY - 1) / BKEY;
+  // tiles past the end reload the last one into an idle slot (never read)
+  auto dma_k = [&](int t, uint16_t* sk) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wave * 16 + 4 * j + prow;
-      const uint32_t key = (uint32_t)min(t * BKEY + r, N - 1);
-      const int slab = (wave * 16 + 4 * j) * HD;
-      __builtin_amdgcn_global_load_lds(kbase + (key * row_bytes + kch[j]), (lds_ptr)(sk + slab), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + (key * row_bytes + vch[j]), (lds_ptr)(sv + slab), 16, 0, 0);
+    for (int j = 0; j < LPW; ++j) {
+      const int r = wave * 4 * LPW + 4 * j + prow;
+      const uint32_t key = (uint32_t)min(min(t, ntiles - 1) * BKEY + r, N - 1);
+      __builtin_amdgcn_global_load_lds(kbase + (key * row_bytes + kch(j)),
+                                       (lds_ptr)(sk + (wave * 4 * LPW + 4 * j) * HD), 16, 0, 0);
+    }
+  };
+  auto dma_v = [&](int t, uint16_t* sv) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int r = wave * 4 * LPW + 4 * j + prow;
+      const uint32_t key = (uint32_t)min(min(t, ntiles - 1) * BKEY + r, N - 1);
+      __builtin_amdgcn_global_load_lds(vbase + (key * row_bytes + vch(j)),
+                                       (lds_ptr)(sv + (wave * 4 * LPW + 4 * j) * HD), 16, 0, 0);
     }
   };
 
@@ -148,43 +178,38 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   float m_run = -INFINITY;  // running max, already multiplied by c
   float l_run = 0.f;
 
-  const int ntiles = (N + BKEY - 1) / BKEY;
-  const bool ragged = (N % BKEY) != 0;
-
-  auto tile = [&](int t, const uint16_t* sk, const uint16_t* sv, uint16_t* nk, uint16_t* nv) {
-    // the last tile reloads itself into the idle buffer (never read)
-    dma(min(t + 1, ntiles - 1), nk, nv);
+  // S^T = K Q^T for one key tile: 2 key blocks of 32, 8 k steps of 16 dims.
+  // MFMA i (st = i / 2, kb = i % 2) alternates the two blocks' chains so
+  // neither waits on itself; its K fragment was read one MFMA earlier.
+  auto kfrag = [&](const char* skb, int i) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(skb + (i & 1) * 32 * 256 + koff[i >> 1]);
+  };
+  auto qk = [&](const uint16_t* sk, f32x16 (&sc)[2]) __attribute__((always_inline)) {
     const char* skb = reinterpret_cast<const char*>(sk);
-    const char* svb = reinterpret_cast<const char*>(sv);
-
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(skb + kb * 32 * 256 + koff[st]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
-      }
-    }
-
-    if (ragged && t == ntiles - 1) {  // keys past N get no weight
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t * BKEY + 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7);
-          if (key >= N) s[kb][r] = -INFINITY;
-        }
-    }
-
-    float mx = s[0][0];
+    bf16x8 fk[2];
+    fk[0] = kfrag(skb, 0);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + 1 < 16) fk[(i + 1) & 1] = kfrag(skb, i + 1);
+      sc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[i & 1], qf[i >> 1], sc[i & 1], 0, 0, 0);
+    }
+  };
+  // row max of a tile's scores, times c.  In the last tile of a ragged N the
+  // keys past N are copies of key N - 1 (the loads clamp), so they do not
+  // change the max and need no mask here.
+  auto row_max = [&](const f32x16 (&sc)[2]) __attribute__((always_inline)) {
+    float mx = sc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    return fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+  };
+  auto rescale = [&](float mx) __attribute__((always_inline)) {
     if (__any(mx > m_run + RESCALE_LOG2)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -195,43 +220,122 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
     }
-
-    bf16x8 pb[4];
+  };
+  // P = exp2(S c - m) in bf16 for the PV MFMA; with `lim` < 64 keys at local
+  // index >= lim get no weight (the last tile of a ragged N)
+  auto softmax = [&](const f32x16 (&sc)[2], bf16x8 (&pb)[4], int lim) __attribute__((always_inline)) {
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_run));
+        float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, -m_run));
+        if (lim < BKEY && 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7) >= lim) p = 0.f;
         psum += p;
         pb[2 * kb + (r >> 3)][r & 7] = (__bf16)p;
       }
     l_run += psum;
-
-    // O^T += V^T P^T; the A operand (8 keys of one dim) is two transposing reads
+  };
+  // O^T += V^T P^T.  The A operand of MFMA i (ks = i / 4, d = i % 4), 8 keys
+  // of one dim per lane, is two transposing reads issued one MFMA earlier.
+  auto vfrag = [&](const char* svb, int i) __attribute__((always_inline)) {
+    const char* base = svb + (i >> 2) * 16 * 256 + voff[i & 3];
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(base));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(base + 4 * 256));
+    const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, both);
+  };
+  auto pv = [&](const uint16_t* sv, const bf16x8 (&pb)[4]) __attribute__((always_inline)) {
+    const char* svb = reinterpret_cast<const char*>(sv);
+    bf16x8 fv[2];
+    fv[0] = vfrag(svb, 0);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const char* base = svb + ks * 16 * 256 + voff[d];
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(base));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(base + 4 * 256));
-        const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[ks],
-                                                         acc[d], 0, 0, 0);
-      }
+    for (int i = 0; i < 16; ++i) {
+      if (i + 1 < 16) fv[(i + 1) & 1] = vfrag(svb, i + 1);
+      acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[i & 1], pb[i >> 2], acc[i & 3], 0, 0, 0);
     }
-    wait_vm();
-    __syncthreads();
   };
 
-  dma(0, s_k0, s_v0);
-  wait_vm();
-  __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
-    tile(t, s_k0, s_v0, s_k1, s_v1);
-    if (t + 1 < ntiles) tile(t + 1, s_k1, s_v1, s_k0, s_v0);
+  // Software pipeline over key tiles.  Iteration t holds S(t) and its row
+  // max; it computes S(t + 1) = K(t + 1) Q^T while the softmax of S(t) runs
+  // (MFMA and VALU of one wave overlap), then O += V(t) P(t) while the row
+  // max of S(t + 1) runs.  K and V have separate 2-slot LDS rings: K(t + 3)
+  // is loaded once every wave has read K(t + 1) (barrier B1), V(t + 2) once
+  // every wave has read V(t) (barrier B2), so each load has about 1.5
+  // iterations to land.  Before B2 a wave waits for K(t + 2) and V(t + 1);
+  // only its K(t + 3) loads (the youngest LPW) may still fly.  The last tile
+  // (softmax with the ragged-N mask, then PV) is peeled off the loop.
+  uint16_t* const ring_k[2] = {s_k0, s_k1};
+  uint16_t* const ring_v[2] = {s_v0, s_v1};
+  f32x16 sa[2], sb[2];
+  bf16x8 pb[4];
+  float mx_a, mx_b;
+
+  dma_k(0, s_k0);
+  dma_v(0, s_v0);
+  dma_k(1, s_k1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm_lpw());
+  barrier_keep_loads();
+  qk(s_k0, sa);
+  mx_a = row_max(sa);
+  dma_v(1, s_v1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm_lpw());
+  barrier_keep_loads();
+  dma_k(2, s_k0);
+
+  // `slot` is t % 2 as a compile-time constant, so every LDS access names
+  // its array statically (the compiler then never waits on the loads in
+  // flight into the other slots)
+  auto iter = [&](auto slot, int t, f32x16 (&cur)[2], float mx_cur, f32x16 (&nxt)[2],
+                  float& mx_nxt) __attribute__((always_inline)) {
+    constexpr int sl = decltype(slot)::value;
+    rescale(mx_cur);
+    // step 1: S(t + 1) MFMAs with softmax(t) VALU
+    qk(ring_k[sl ^ 1], nxt);
+    softmax(cur, pb, BKEY);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // first K fragment
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next K fragment
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // 7 VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    barrier_keep_loads();  // B1
+    dma_k(t + 3, ring_k[sl ^ 1]);
+    // step 2: O += V(t) P(t) with the row max of S(t + 1)
+    pv(ring_v[sl], pb);
+    mx_nxt = row_max(nxt);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // first V fragment
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next V fragment
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // 1 VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm_lpw());
+    barrier_keep_loads();  // B2
+    dma_v(t + 2, ring_v[sl]);
+  };
+  auto last = [&](auto slot, f32x16 (&cur)[2], float mx_cur) __attribute__((always_inline)) {
+    constexpr int sl = decltype(slot)::value;
+    rescale(mx_cur);
+    softmax(cur, pb, N - (ntiles - 1) * BKEY);
+    pv(ring_v[sl], pb);
+  };
+  int t = 0;
+  for (; t + 2 < ntiles; t += 2) {
+    iter(std::integral_constant<int, 0>{}, t, sa, mx_a, sb, mx_b);
+    iter(std::integral_constant<int, 1>{}, t + 1, sb, mx_b, sa, mx_a);
   }
+  if (t + 1 < ntiles) {
+    iter(std::integral_constant<int, 0>{}, t, sa, mx_a, sb, mx_b);
+    last(std::integral_constant<int, 1>{}, sb, mx_b);
+  } else {
+    last(std::integral_constant<int, 0>{}, sa, mx_a);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm0());
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
@@ -254,7 +358,7 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        int N, int H, int ld_qkv, int ld_o, float softmax_scale,
                        hipStream_t stream) {
   const int nqt = (N + BQ - 1) / BQ;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(nqt * H), dim3(256), 0, stream, q, k, v, o, N, H,
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(nqt * H), dim3(64 * NWAVE), 0, stream, q, k, v, o, N, H,
                      ld_qkv, ld_o, softmax_scale * DIT_LOG2E);
   return hipGetLastError();
 }

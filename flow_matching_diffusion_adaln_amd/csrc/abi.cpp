@@ -127,14 +127,14 @@ int block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const 
                                          stream))))
     return rc;
   if ((rc = mark(DIT_STAGE_GEMM_IN))) return rc;
-  if ((rc = hip_status(dit::launch_gemm_in(w.u, static_cast<const uint16_t*>(w_in), s.N, s.D,
-                                           s.F, w.q, w.k, w.v, w.cat, w.partial, stream))))
+  // the input projection applies the QK RMSNorm and RoPE in its epilogue, so
+  // the rope stage is empty here (its events bracket no work)
+  if ((rc = hip_status(dit::launch_gemm_in(
+           w.u, static_cast<const uint16_t*>(w_in), s.N, s.D, s.F, w.q, w.k, w.v, w.cat, pos,
+           static_cast<const uint16_t*>(q_scale), static_cast<const uint16_t*>(k_scale),
+           desc->rope_theta, desc->qk_eps, w.partial, stream))))
     return rc;
   if ((rc = mark(DIT_STAGE_ROPE))) return rc;
-  if ((rc = hip_status(dit::launch_rope4(w.q, w.k, pos, static_cast<const uint16_t*>(q_scale),
-                                         static_cast<const uint16_t*>(k_scale), s.N, s.H,
-                                         desc->rope_theta, desc->qk_eps, stream))))
-    return rc;
   if ((rc = mark(DIT_STAGE_ATTN))) return rc;
   if ((rc = hip_status(dit::launch_attn(w.q, w.k, w.v, w.cat, s.N, s.H, s.D, s.D + s.F,
                                         1.0f / sqrtf((float)DIT_HEAD_DIM), stream))))

@@ -55,6 +55,12 @@ struct GemmArgs {
   uint16_t* k;
   uint16_t* v;
   uint16_t* cat;      // [M, D + F]; m goes to columns [D, D + F)
+  // per-head QK RMSNorm + 4-axis RoPE applied to q and k in the epilogue
+  const int32_t* pos;      // [M, 4] (t, h, w, l)
+  const uint16_t* q_scale;  // [128] bf16
+  const uint16_t* k_scale;  // [128] bf16
+  float qk_eps;
+  double rope_rev[16];     // theta^(-2j / 32) / (2 pi): turns per position step of pair j
   // output projection
   const uint16_t* x;  // residual [M, D]
   const uint16_t* mod;  // [S, 3, D]
@@ -125,7 +131,11 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+// silu(a) = a / (1 + e^-a) with the hardware reciprocal (about 1 ulp; the
+// result is rounded to bf16), not the IEEE division sequence
+__device__ __forceinline__ float silu(float a) {
+  return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
 
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   return make_uint2(pack2(a, b), pack2(c, d));
@@ -193,11 +203,96 @@ __device__ __forceinline__ void epilogue_pair(const GemmArgs& g, int tm, int tn,
   }
 }
 
+// q / k tile epilogue of the 256-row layout: per-head RMSNorm with the
+// learnable scale, then 4-axis RoPE, straight from the fp32 accumulators
+// (the same operations the standalone rope4 kernel applies to stored q, k).
+// Wave (wm, wn) holds columns [128 wn, 128 wn + 128) of the tile, i.e. one
+// whole head, and in block j = 0..3 the 32 dims of axis j; lane (ln, hl)
+// holds, for each row, dims 8 rr + 4 hl + e of every axis, the other half
+// sits in lane ln ^ 32.  Pair p of an axis is dims (2 p, 2 p + 1), turned by
+// pos_axis * theta^(-2 p / 32) radians.
+__device__ __forceinline__ void epilogue_qk(const GemmArgs& g, const f32x16 (&acc)[4][4], int tm,
+                                            int tn, int wm, int wn, int lane) {
+  constexpr int BM = 256, MB = 4, NB = 4;
+  const int ln = lane & 31, hl = lane >> 5;
+  const int which = tn * BN / g.D;  // 0: q, 1: k
+  uint16_t* const dst = which ? g.k : g.q;
+  const uint16_t* const scale = which ? g.k_scale : g.q_scale;
+  const int c0 = tn * BN - which * g.D + wn * NB * 32;  // first dim of the head
+  // Per-lane inputs, all loads issued before the first use: the scale of
+  // this lane's 64 dims, the turn rate of its 8 pairs per axis, and the
+  // positions of its 4 rows.
+  uint2 gsc[NB][4];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      gsc[j][rr] = *reinterpret_cast<const uint2*>(scale + j * 32 + 8 * rr + 4 * hl);
+  double fr[4][2];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const double f0 = g.rope_rev[4 * rr + pr], f1 = g.rope_rev[4 * rr + 2 + pr];
+      fr[rr][pr] = hl ? f1 : f0;
+    }
+  int4 p4[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int row = tm * BM + (wm * MB + i) * 32 + ln;
+    p4[i] = reinterpret_cast<const int4*>(g.pos)[min(row, g.M - 1)];
+  }
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int row = tm * BM + (wm * MB + i) * 32 + ln;
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ss = fmaf(acc[i][j][r], acc[i][j][r], ss);
+    ss += __shfl_xor(ss, 32, 64);
+    const float rstd = rsqrtf(ss * (1.0f / 128.0f) + g.qk_eps);
+    if (row >= g.M) continue;
+    const int pa[4] = {p4[i].x, p4[i].y, p4[i].z, p4[i].w};
+    uint16_t* const dr = dst + (size_t)row * g.D + c0 + 4 * hl;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const double pj = (double)pa[j];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const uint2 gs = gsc[j][rr];
+        const float x[4] = {acc[i][j][4 * rr] * rstd * lo2f(gs.x),
+                            acc[i][j][4 * rr + 1] * rstd * hi2f(gs.x),
+                            acc[i][j][4 * rr + 2] * rstd * lo2f(gs.y),
+                            acc[i][j][4 * rr + 3] * rstd * hi2f(gs.y)};
+        float y[4];
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          // pair 4 rr + 2 hl + pr of axis j; the turn count is reduced to
+          // [0, 1) in double, then sin / cos of 2 pi r in hardware
+          const double t = pj * fr[rr][pr];
+          const float r = (float)(t - floor(t));
+          const float sn = __builtin_amdgcn_sinf(r), cs = __builtin_amdgcn_cosf(r);
+          y[2 * pr] = x[2 * pr] * cs - x[2 * pr + 1] * sn;
+          y[2 * pr + 1] = x[2 * pr] * sn + x[2 * pr + 1] * cs;
+        }
+        *reinterpret_cast<uint2*>(dr + j * 32 + 8 * rr) = pack4(y[0], y[1], y[2], y[3]);
+      }
+    }
+  }
+}
+
 template <int EPI, int BM>
 __device__ __forceinline__ void epilogue(const GemmArgs& g,
                                          const f32x16 (&acc)[Tile<BM>::MB][Tile<BM>::NB], int tm,
                                          int tn, int wm, int wn, int lane) {
   constexpr int MB = Tile<BM>::MB, NB = Tile<BM>::NB;
+  if constexpr (EPI == EPI_IN && BM == 256) {
+    if (tn < 2 * g.D / BN) {  // q or k
+      epilogue_qk(g, acc, tm, tn, wm, wn, lane);
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -570,30 +665,41 @@ Plan pick_plan(int M, int K, int num_n, bool can_split) {
 
 template <int EPI>
 hipError_t launch(GemmArgs g, hipStream_t stream) {
-  const Plan p = pick_plan(g.M, g.K, g.num_n, g.partial != nullptr);
-  const int bm = p.bm;
+  const bool can_split = g.partial != nullptr;
+  Plan p;
+  if constexpr (EPI == EPI_IN) {
+    // 256-row tiles only: the q / k epilogue needs a whole head per wave.
+    // Split tail tiles end in the fix-up kernel, whose epilogue does not
+    // normalize or rotate, so a tail must hold no q or k tile (tail tiles are
+    // the last in tile order, i.e. the highest N tiles: MLP ones).
+    p = make_plan(256, g.M, g.K, g.num_n, can_split);
+    const int num_m = (g.M + 255) / 256;
+    if (p.n_tail && (p.n_dp / (GROUP_N * num_m)) * GROUP_N < 2 * g.D / BN)
+      p = make_plan(256, g.M, g.K, g.num_n, false);
+  } else {
+    p = pick_plan(g.M, g.K, g.num_n, can_split);
+  }
   g.n_dp = p.n_dp;
   g.n_tail = p.n_tail;
   g.n_pieces = p.n_pieces;
   g.unit = unroll_period(g.K);
   const int grid = g.n_dp + (g.n_tail ? g.n_pieces : 0);
-  if (g.unit == 6) {
-    if (bm == 224)
-      hipLaunchKernelGGL((gemm_kernel<EPI, 224, 3>), dim3(grid), dim3(256), 0, stream, g);
-    else
+  const bool tall = EPI == EPI_IN || p.bm == 256;
+  if (tall) {
+    if (g.unit == 6)
       hipLaunchKernelGGL((gemm_kernel<EPI, 256, 3>), dim3(grid), dim3(256), 0, stream, g);
-  } else {
-    if (bm == 224)
-      hipLaunchKernelGGL((gemm_kernel<EPI, 224, 2>), dim3(grid), dim3(256), 0, stream, g);
     else
       hipLaunchKernelGGL((gemm_kernel<EPI, 256, 2>), dim3(grid), dim3(256), 0, stream, g);
-  }
-  if (g.n_tail) {
-    if (bm == 224)
-      hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 224>), dim3(g.n_tail * 224 * BN / 8 / 256),
-                         dim3(256), 0, stream, g);
-    else
+    if (g.n_tail)
       hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 256>), dim3(g.n_tail * 256 * BN / 8 / 256),
+                         dim3(256), 0, stream, g);
+  } else if constexpr (EPI == EPI_OUT) {
+    if (g.unit == 6)
+      hipLaunchKernelGGL((gemm_kernel<EPI, 224, 3>), dim3(grid), dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((gemm_kernel<EPI, 224, 2>), dim3(grid), dim3(256), 0, stream, g);
+    if (g.n_tail)
+      hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 224>), dim3(g.n_tail * 224 * BN / 8 / 256),
                          dim3(256), 0, stream, g);
   }
   return hipGetLastError();
@@ -602,9 +708,16 @@ hipError_t launch(GemmArgs g, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D, int F,
-                          uint16_t* q, uint16_t* k, uint16_t* v, uint16_t* cat, float* partial,
-                          hipStream_t stream) {
+                          uint16_t* q, uint16_t* k, uint16_t* v, uint16_t* cat,
+                          const int32_t* pos, const uint16_t* q_scale, const uint16_t* k_scale,
+                          float theta, float qk_eps, float* partial, hipStream_t stream) {
   GemmArgs g{};
+  g.pos = pos;
+  g.q_scale = q_scale;
+  g.k_scale = k_scale;
+  g.qk_eps = qk_eps;
+  const double two_pi = 6.283185307179586;
+  for (int j = 0; j < 16; ++j) g.rope_rev[j] = pow((double)theta, -2.0 * j / 32.0) / two_pi;
   g.partial = partial;
   g.A = u;
   g.W = w_in;

@@ -25,8 +25,9 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        hipStream_t stream);
 
 hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D, int F,
-                          uint16_t* q, uint16_t* k, uint16_t* v, uint16_t* cat, float* partial,
-                          hipStream_t stream);
+                          uint16_t* q, uint16_t* k, uint16_t* v, uint16_t* cat,
+                          const int32_t* pos, const uint16_t* q_scale, const uint16_t* k_scale,
+                          float theta, float qk_eps, float* partial, hipStream_t stream);
 
 hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, int D, int F,
                            const uint16_t* x, const uint16_t* mod, uint16_t* y, int e0, int e1,

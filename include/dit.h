@@ -67,8 +67,9 @@ enum {
 
 /* Stages of dit_block_fwd, in launch order (see dit_block_fwd_events). */
 #define DIT_STAGE_ADALN 0    /* per-stream AdaLN -> u                           */
-#define DIT_STAGE_GEMM_IN 1  /* u W_in^T -> q, k, v and SwiGLU m                */
-#define DIT_STAGE_ROPE 2     /* QK RMSNorm + 4-axis RoPE on q, k                */
+#define DIT_STAGE_GEMM_IN 1  /* u W_in^T -> q, k, v and SwiGLU m, with the QK    */
+                             /* RMSNorm + 4-axis RoPE of q, k in its epilogue   */
+#define DIT_STAGE_ROPE 2     /* empty: the RoPE is fused into the stage above   */
 #define DIT_STAGE_ATTN 3     /* joint attention -> o                            */
 #define DIT_STAGE_GEMM_OUT 4 /* [o | m] W_out^T, gated residual -> y            */
 #define DIT_N_STAGES 5

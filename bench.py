@@ -217,7 +217,8 @@ def main():
         "adaln_gbs": round(4.0 * cfg.N * D / (st["adaln"] * 1e-3) / 1e9, 1),
         "rope_gbs": round(8.0 * cfg.N * D / (st["rope"] * 1e-3) / 1e9, 1),
         "roofline": {
-            "kernel": "gemm_kernel<EPI_IN> (fused q|k|v|SwiGLU input projection)",
+            "kernel": "input projection: gemm_kernel<EPI_IN> (q|k|v|SwiGLU, QK RMSNorm + RoPE "
+                      "epilogue) + its split-tail fix-up, timed together",
             "bound": "mfma",
             "achieved": round(gemm_in_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,

@@ -7,3 +7,4 @@ from .dit_block import (  # noqa: F401
     FLAG_NO_GATE, FLAG_NO_RESIDUAL, adaln_ref, attention_ref, block_ref, head_rms_norm,
     layer_norm, rel_l2, rope4_ref, rope_omega, silu, softmax_rows, stream_index, swiglu_ref,
     widen_bf16)
+from .stack import cfg_combine, round_bf16, stack_branch, stack_cfg_ref  # noqa: F401

@@ -9,7 +9,8 @@ between steps so the 245 MB of one block's weights is not served from the
 steps gives per-stage times from HIP events the library records on the work
 stream between its kernels.  The fp64 CPU oracle of the same block
 is timed once on the host as a baseline and its output gives the parity of
-the timed configuration.
+the timed configuration.  A secondary field times one guided denoise step of
+the two-stage stack (c5) through dit_stack_fwd (`--no-stack` skips it).
 
 Prints one JSON line.
 """
@@ -39,6 +40,8 @@ def parse():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--weight-sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the secondary measurement of the two-stage stack with CFG (c5)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the timed steps "
                          "(reference point for the profiler's FETCH_SIZE / WRITE_SIZE)")
@@ -90,6 +93,61 @@ def cpu_baseline(d, cfg):
         sec = time.perf_counter() - t0
     blas = ",".join(sorted({i.get("internal_api", "?") for i in info})) or "?"
     return ref, sec, threads, blas
+
+
+def stack_c5(torch, configs, ops, steps: int, warmup: int) -> dict:
+    """Secondary measurement: one guided denoise step of the two-stage stack
+    (5 image + 5 text stage-1 blocks, 28 joint blocks, CFG scale 4) through
+    dit_stack_fwd, each block with its own random weights generated on the
+    device (38 sets, 9.3 GB).  The image stage-1 blocks are shared by both
+    guidance branches, so the executed FLOPs are below two full forwards."""
+    sc = configs.C5
+    D, F, d = configs.WIDTH, configs.MLP_HIDDEN, configs.HEAD_DIM
+    n_img, n_txt = sc.image_side * sc.image_side, sc.n_text
+    gen = torch.Generator(device="cuda").manual_seed(4321)
+
+    def rnd(shape, std):
+        return (torch.randn(shape, generator=gen, device="cuda") * std).to(torch.bfloat16)
+
+    ones = torch.ones(d, dtype=torch.bfloat16, device="cuda")
+    blocks = []
+    for i in range(2 * sc.n_stage1 + sc.n_joint):
+        s = 1 if i < 2 * sc.n_stage1 else 2
+        blocks.append({"mod": rnd((s, 3, D), 0.1 ** 0.5), "w_in": rnd((3 * D + 2 * F, D), D ** -0.5),
+                       "w_out": rnd((D, D + F), (D + F) ** -0.5), "q_scale": ones, "k_scale": ones})
+    cfg_img = configs.BlockConfig("img", 0, (configs.Stream("image", n_img, (sc.image_side,) * 2, sc.t),))
+    cfg_txt = configs.BlockConfig("txt", 0, (configs.Stream("text", n_txt),))
+    cfg_joint = configs.BlockConfig("joint", 0, (configs.Stream("image", n_img, (sc.image_side,) * 2, sc.t),
+                                                 configs.Stream("text", n_txt)))
+    x_img = rnd((n_img, D), 1.0)
+    x_c, x_n = rnd((n_txt, D), 1.0), rnd((n_txt, D), 1.0)
+    from flow_matching_diffusion_adaln_amd import inputs
+    pos = torch.from_numpy(inputs.positions(cfg_joint)).cuda()
+    desc = ops.make_stack_desc(n_img, n_txt, sc.n_stage1, sc.n_stage1, sc.n_joint, sc.cfg_scale)
+    ws = torch.empty(ops.stack_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    v = torch.empty((n_img, D), dtype=torch.bfloat16, device="cuda")
+    for _ in range(warmup):
+        ops.stack_fwd(desc, x_img, x_c, x_n, pos, blocks, v_img=v, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ops.stack_fwd(desc, x_img, x_c, x_n, pos, blocks, v_img=v, workspace=ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    flop_exec = (sc.n_stage1 * cfg_img.flop() + 2 * sc.n_stage1 * cfg_txt.flop()
+                 + 2 * sc.n_joint * cfg_joint.flop())
+    flop_nominal = 2 * sc.n_stage1 * (cfg_img.flop() + cfg_txt.flop()) + 2 * sc.n_joint * cfg_joint.flop()
+    assert bool(torch.isfinite(v.float()).all())
+    return {
+        "workload": f"c5: {sc.n_stage1} image ({n_img} tokens) + {sc.n_stage1} text ({n_txt}) "
+                    f"stage-1 blocks, {sc.n_joint} joint blocks ({n_img + n_txt}), CFG pair "
+                    f"(scale {sc.cfg_scale}); image stage-1 shared by both branches",
+        "ms_per_denoise_step": round(ms, 3),
+        "tflops_executed": round(flop_exec / (ms * 1e-3) / 1e12, 2),
+        "gflop_executed": round(flop_exec / 1e9, 1),
+        "gflop_two_full_forwards": round(flop_nominal / 1e9, 1),
+        "steps": steps, "warmup": warmup,
+    }
 
 
 def main():
@@ -231,6 +289,9 @@ def main():
         "device": dev_name,
         "input_gen_s": round(t_gen, 1),
     }
+
+    if not args.no_stack:
+        result["stack_c5"] = stack_c5(torch, configs, ops, steps=3, warmup=1)
 
     if not args.no_cpu_baseline:
         ref, sec, threads, blas = cpu_baseline(d, cfg)

@@ -33,4 +33,8 @@ hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, in
                            const uint16_t* x, const uint16_t* mod, uint16_t* y, int e0, int e1,
                            uint32_t flags, float* partial, hipStream_t stream);
 
+// out = neg + scale * (cond - neg) elementwise over n bf16 values (n a multiple of 8)
+hipError_t launch_cfg_combine(const uint16_t* cond, const uint16_t* neg, uint16_t* out,
+                              long long n, float scale, hipStream_t stream);
+
 }  // namespace dit

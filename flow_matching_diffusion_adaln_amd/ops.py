@@ -23,7 +23,8 @@ DIT_F_NO_GATE = 2
 N_STAGES = 5
 STAGES = ("adaln", "gemm_in", "rope", "attn", "gemm_out")
 EXPORTS = ("dit_block_workspace_bytes", "dit_block_fwd", "dit_block_fwd_events", "dit_attn_fwd",
-           "rope4_apply", "adaln_mod", "dit_status_str")
+           "rope4_apply", "adaln_mod", "dit_stack_workspace_bytes", "dit_stack_fwd",
+           "dit_status_str")
 
 
 class BlockDesc(ctypes.Structure):
@@ -39,6 +40,28 @@ class BlockDesc(ctypes.Structure):
         ("qk_eps", ctypes.c_float),
         ("flags", ctypes.c_uint32),
     ]
+
+
+class StackDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_img", ctypes.c_int32),
+        ("n_txt", ctypes.c_int32),
+        ("n_img_blocks", ctypes.c_int32),
+        ("n_txt_blocks", ctypes.c_int32),
+        ("n_joint_blocks", ctypes.c_int32),
+        ("width", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("mlp_hidden", ctypes.c_int32),
+        ("rope_theta", ctypes.c_float),
+        ("ln_eps", ctypes.c_float),
+        ("qk_eps", ctypes.c_float),
+        ("cfg_scale", ctypes.c_float),
+    ]
+
+
+class BlockParams(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in ("mod", "w_in", "w_out", "q_scale", "k_scale")]
 
 
 _lib = None
@@ -60,6 +83,10 @@ def load_library() -> ctypes.CDLL:
     lib.dit_attn_fwd.argtypes = [i32, i32, i32, vp, vp, vp, vp, f32, vp]
     lib.rope4_apply.argtypes = [i32, i32, i32, vp, vp, vp, f32, vp, vp, f32, vp]
     lib.adaln_mod.argtypes = [i32, ctypes.POINTER(i32), i32, vp, vp, vp, f32, vp]
+    stack_p = ctypes.POINTER(StackDesc)
+    lib.dit_stack_workspace_bytes.argtypes = [stack_p, ctypes.POINTER(sz)]
+    lib.dit_stack_fwd.argtypes = [stack_p, vp, vp, vp, vp, ctypes.POINTER(BlockParams), vp, vp,
+                                  sz, vp]
     lib.dit_status_str.argtypes = [ctypes.c_int]
     lib.dit_status_str.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -216,3 +243,61 @@ def to_host_bits(t: torch.Tensor):
     """bfloat16 GPU tensor -> uint16 numpy bit patterns."""
     import numpy as np
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def make_stack_desc(n_img: int, n_txt: int, n_img_blocks: int, n_txt_blocks: int,
+                    n_joint_blocks: int, cfg_scale: float, width: int = configs.WIDTH,
+                    n_heads: int = configs.N_HEADS, head_dim: int = configs.HEAD_DIM,
+                    mlp_hidden: int = configs.MLP_HIDDEN) -> StackDesc:
+    d = StackDesc()
+    d.n_img, d.n_txt = n_img, n_txt
+    d.n_img_blocks, d.n_txt_blocks, d.n_joint_blocks = n_img_blocks, n_txt_blocks, n_joint_blocks
+    d.width, d.n_heads, d.head_dim, d.mlp_hidden = width, n_heads, head_dim, mlp_hidden
+    d.rope_theta, d.ln_eps, d.qk_eps = configs.ROPE_THETA, configs.LN_EPS, configs.QK_EPS
+    d.cfg_scale = cfg_scale
+    return d
+
+
+def stack_workspace_bytes(desc: StackDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().dit_stack_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def stack_fwd(desc: StackDesc, x_img, x_txt_cond, x_txt_neg, pos, blocks, v_img=None,
+              workspace=None, stream=None) -> torch.Tensor:
+    """v_img = dit_stack_fwd(...).  blocks: sequence of dicts with keys mod,
+    w_in, w_out, q_scale, k_scale (image blocks, then text, then joint)."""
+    D, F, d = desc.width, desc.mlp_hidden, desc.head_dim
+    N = desc.n_img + desc.n_txt
+    _bf16(x_img, (desc.n_img, D), "x_img")
+    _bf16(x_txt_cond, (desc.n_txt, D), "x_txt_cond")
+    if x_txt_neg is not None:
+        _bf16(x_txt_neg, (desc.n_txt, D), "x_txt_neg")
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (N, 4) or not pos.is_cuda \
+            or not pos.is_contiguous():
+        raise ValueError("pos must be a contiguous int32 [n_img + n_txt, 4] GPU tensor")
+    n_blocks = desc.n_img_blocks + desc.n_txt_blocks + desc.n_joint_blocks
+    if len(blocks) != n_blocks:
+        raise ValueError(f"expected {n_blocks} blocks, got {len(blocks)}")
+    arr = (BlockParams * max(n_blocks, 1))()
+    for i, b in enumerate(blocks):
+        s = 1 if i < desc.n_img_blocks + desc.n_txt_blocks else 2
+        _bf16(b["mod"], (s, 3, D), f"blocks[{i}].mod")
+        _bf16(b["w_in"], (3 * D + 2 * F, D), f"blocks[{i}].w_in")
+        _bf16(b["w_out"], (D, D + F), f"blocks[{i}].w_out")
+        _bf16(b["q_scale"], (d,), f"blocks[{i}].q_scale")
+        _bf16(b["k_scale"], (d,), f"blocks[{i}].k_scale")
+        for name in ("mod", "w_in", "w_out", "q_scale", "k_scale"):
+            setattr(arr[i], name, b[name].data_ptr())
+    if v_img is None:
+        v_img = torch.empty((desc.n_img, D), dtype=torch.bfloat16, device=x_img.device)
+    _bf16(v_img, (desc.n_img, D), "v_img")
+    if workspace is None:
+        workspace = torch.empty(stack_workspace_bytes(desc), dtype=torch.uint8,
+                                device=x_img.device)
+    _check(load_library().dit_stack_fwd(
+        ctypes.byref(desc), _ptr(x_img), _ptr(x_txt_cond), _ptr(x_txt_neg),
+        ctypes.c_void_p(pos.data_ptr()), arr, _ptr(v_img), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return v_img

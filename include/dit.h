@@ -87,8 +87,9 @@ typedef struct dit_block_desc {
   uint32_t flags;                    /* DIT_F_* bits, 0 for the block itself               */
 } dit_block_desc;
 
-/* Bytes of device workspace dit_block_fwd needs for `desc` (about 49 * N * D
- * bytes at F = 3 D: u, q, k, v and the [o | m] concat buffer, all bf16). */
+/* Bytes of device workspace dit_block_fwd needs for `desc`: u, q, k, v and the
+ * [o | m] concat buffer, all bf16 (16 * N * D bytes at F = 3 D), plus a fixed
+ * 128 MiB of fp32 scratch for the split tails of the GEMMs. */
 int dit_block_workspace_bytes(const dit_block_desc* desc, size_t* bytes);
 
 /* One parallel block forward (the whole chain above).
@@ -149,6 +150,64 @@ int rope4_apply(int32_t n_tokens, int32_t n_heads, int32_t head_dim, void* q, vo
  * width must be a multiple of 512 and at most 8192. */
 int adaln_mod(int32_t n_streams, const int32_t* n_tokens, int32_t width, const void* x,
               const void* mod, void* out, float eps, hipStream_t stream);
+
+/* ---- Two-stage stack and classifier-free guidance -------------------------
+ * One denoise step of the transformer ("Welcome FLUX.3 Image Klein in
+ * Diffusers", section "How it works": each stream first runs through blocks of
+ * its own, attending only to itself, then the streams are concatenated and
+ * run through the shared joint blocks; the miles page "FLUX 3 Image Klein",
+ * section 3: the guided prediction is neg + scale * (pos - neg) from a forward
+ * with the prompt and one with the negative prompt).  Every block is the
+ * parallel block of dit_block_fwd.  Embedders and output layers are not part
+ * of this call: image and text tokens enter as given, and the guided result
+ * is taken on the image rows of the joint stack's output. */
+typedef struct dit_stack_desc {
+  int32_t n_img;          /* image tokens (> 0)                                    */
+  int32_t n_txt;          /* text tokens of each branch (> 0)                      */
+  int32_t n_img_blocks;   /* stage-1 image blocks (5)                              */
+  int32_t n_txt_blocks;   /* stage-1 text blocks (5)                               */
+  int32_t n_joint_blocks; /* stage-2 joint blocks over [image | text] (28)         */
+  int32_t width;          /* D, 3072                                               */
+  int32_t n_heads;        /* H, 24                                                 */
+  int32_t head_dim;       /* 128                                                   */
+  int32_t mlp_hidden;     /* F, 9216                                               */
+  float rope_theta;       /* 10000                                                 */
+  float ln_eps;           /* 1e-6                                                  */
+  float qk_eps;           /* 1e-6                                                  */
+  float cfg_scale;        /* guidance scale, finite; 1 runs the conditional branch */
+                          /* only (no negative forward)                           */
+} dit_stack_desc;
+
+/* Device pointers of one block's parameters. */
+typedef struct dit_block_params {
+  const void* mod;     /* bf16 [S, 3, D]: S = 1 for a stage-1 block, 2 (image, text) for a joint block */
+  const void* w_in;    /* bf16 [3D + 2F, D], as in dit_block_fwd */
+  const void* w_out;   /* bf16 [D, D + F]  */
+  const void* q_scale; /* bf16 [d]         */
+  const void* k_scale; /* bf16 [d]         */
+} dit_block_params;
+
+/* Bytes of device workspace dit_stack_fwd needs: the block workspace at
+ * N = n_img + n_txt plus two [N, D] bf16 activation buffers (one per branch). */
+int dit_stack_workspace_bytes(const dit_stack_desc* desc, size_t* bytes);
+
+/* One guided stack forward.
+ *   x_img       bf16 [n_img, D]   image tokens entering stage 1
+ *   x_txt_cond  bf16 [n_txt, D]   text tokens of the prompt
+ *   x_txt_neg   bf16 [n_txt, D]   text tokens of the negative prompt (may be
+ *                                 null when cfg_scale == 1)
+ *   pos         int32 [n_img + n_txt, 4]  joint (t, h, w, l) positions, image
+ *                                 rows first; stage-1 blocks use their rows
+ *   blocks      host array of n_img_blocks + n_txt_blocks + n_joint_blocks
+ *               entries: image blocks, then text blocks, then joint blocks
+ *   v_img       bf16 [n_img, D]   out: neg + cfg_scale * (cond - neg) on the
+ *                                 image rows of the joint output, in fp32, rounded
+ *                                 to bf16 (the cond rows when cfg_scale == 1)
+ * The stage-1 image blocks do not see the text, so both branches share them.
+ * Activations between blocks are bf16, as in dit_block_fwd. */
+int dit_stack_fwd(const dit_stack_desc* desc, const void* x_img, const void* x_txt_cond,
+                  const void* x_txt_neg, const int32_t* pos, const dit_block_params* blocks,
+                  void* v_img, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static name of a status code ("DIT_OK", "DIT_ERR_SHAPE: ...", ...). */
 const char* dit_status_str(int status);

@@ -47,7 +47,7 @@ def round_bf16(a: np.ndarray) -> np.ndarray:
     rounded = (bits + np.uint64((1 << 44) - 1) + lsb) & ~np.uint64((1 << 45) - 1)
     out = rounded.view(np.float64)
     # values whose bf16 exponent overflows become inf, as in the bf16 store
-    return np.where(np.abs(out) > 3.3895313892515355e38, np.sign(a) * np.inf, out)
+    return np.where(np.abs(out) > 3.3895313892515355e38, np.copysign(np.inf, a), out)
 
 
 def cfg_combine(cond: np.ndarray, neg: np.ndarray, scale: float) -> np.ndarray:

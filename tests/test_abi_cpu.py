@@ -176,3 +176,70 @@ def test_adaln_host_errors(lib):
     assert f(2, bad, 3072, x, m, o, 1e-6, None) == SHAPE
     empty = (ctypes.c_int32 * 2)(0, 0)
     assert f(2, empty, 3072, None, None, None, 1e-6, None) == OK
+
+
+# ------------------------------------------------------------- dit_stack_* --
+
+def stack_ws(lib, d):
+    n = ctypes.c_size_t(0)
+    rc = lib.dit_stack_workspace_bytes(ctypes.byref(d), ctypes.byref(n))
+    return rc, n.value
+
+
+def test_stack_struct_layout():
+    assert ctypes.sizeof(ops.StackDesc) == 52
+    assert ctypes.sizeof(ops.BlockParams) == 40
+
+
+def test_stack_workspace_bytes(lib):
+    d = ops.make_stack_desc(4096, 160, 5, 5, 28, 4.0)
+    rc, n = stack_ws(lib, d)
+    assert rc == OK
+    rc_b, nb = ws(lib, ops.make_desc([4096, 160]))
+    # the block workspace at N = 4256 plus one [N, D] bf16 buffer per branch
+    assert n == nb + 2 * 4256 * 3072 * 2
+    assert lib.dit_stack_workspace_bytes(None, ctypes.byref(ctypes.c_size_t())) == NULL
+
+
+@pytest.mark.parametrize("field,value,want", [
+    ("n_img", 0, SHAPE), ("n_txt", 0, SHAPE), ("n_img_blocks", -1, SHAPE),
+    ("n_joint_blocks", 2000, SHAPE), ("width", 3000, SHAPE), ("head_dim", 64, SHAPE),
+    ("cfg_scale", float("nan"), ARG), ("qk_eps", -1.0, ARG)])
+def test_stack_desc_validation(lib, field, value, want):
+    d = ops.make_stack_desc(256, 80, 1, 1, 2, 4.0)
+    setattr(d, field, value)
+    assert stack_ws(lib, d)[0] == want
+
+
+def stack_call(lib, d, x_img=P, x_c=P + (1 << 30), x_n=P + (2 << 30), pos=P + (3 << 30),
+               blocks="ok", v=P + (4 << 30), wsp=P + (5 << 30), ws_bytes=None):
+    n_blocks = d.n_img_blocks + d.n_txt_blocks + d.n_joint_blocks
+    arr = (ops.BlockParams * max(n_blocks, 1))()
+    for i in range(n_blocks):
+        for j, name in enumerate(("mod", "w_in", "w_out", "q_scale", "k_scale")):
+            setattr(arr[i], name, P + ((6 + 5 * i + j) << 30))
+    if blocks == "bad_null":
+        arr[n_blocks - 1].w_out = None
+    elif blocks == "bad_align":
+        arr[0].q_scale = BAD
+    if ws_bytes is None:
+        ws_bytes = stack_ws(lib, d)[1]
+    c = ctypes.c_void_p
+    return lib.dit_stack_fwd(ctypes.byref(d), c(x_img) if x_img else None,
+                             c(x_c) if x_c else None, c(x_n) if x_n else None,
+                             c(pos) if pos else None, None if blocks is None else arr,
+                             c(v) if v else None, c(wsp) if wsp else None,
+                             ctypes.c_size_t(ws_bytes), None)
+
+
+def test_stack_fwd_host_errors(lib):
+    d = ops.make_stack_desc(256, 80, 1, 1, 2, 4.0)
+    assert stack_call(lib, d, x_img=0) == NULL
+    assert stack_call(lib, d, x_n=0) == NULL          # guided: the negative branch is needed
+    assert stack_call(lib, d, pos=0) == NULL
+    assert stack_call(lib, d, blocks=None) == NULL
+    assert stack_call(lib, d, blocks="bad_null") == NULL   # the last block is checked up front
+    assert stack_call(lib, d, blocks="bad_align") == ALIGN
+    assert stack_call(lib, d, x_c=BAD) == ALIGN
+    assert stack_call(lib, d, ws_bytes=stack_ws(lib, d)[1] - 1) == WS
+    assert stack_call(lib, d, v=P + (5 << 30)) == ARG      # output inside the workspace

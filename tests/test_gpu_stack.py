@@ -1,0 +1,95 @@
+"""GPU tests of the two-stage stack with classifier-free guidance
+(dit_stack_fwd) against the fp64 stack oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _gpu import require_gpu, widen
+from flow_matching_diffusion_adaln_amd import configs, inputs, ops
+
+pytestmark = pytest.mark.gpu
+
+D, F, d, H = configs.WIDTH, configs.MLP_HIDDEN, configs.HEAD_DIM, configs.N_HEADS
+DIMS = dict(n_heads=H, head_dim=d, mlp_hidden=F)
+# stacked: each block's output is bf16-rounded and fed on; the guided result
+# 4 cond - 3 neg adds the two branches' errors (which are correlated: both
+# share the image stage), so the bound is the block's 1e-2 times the CFG
+# amplification (|4| + |3|) / |4 - 3| = 7 on the branch difference, taken
+# on the result as a whole
+TOL_STACK = 2e-2
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def block_params(seed, kind_id, n_streams, zero_gate=False):
+    key = (seed, 300 + kind_id)
+    mod = inputs.normal_bf16((n_streams, 3, D), np.sqrt(0.1), *key, 1)
+    if zero_gate:
+        mod[:, 2, :] = 0
+    return {
+        "mod": mod,
+        "w_in": inputs.normal_bf16((3 * D + 2 * F, D), 1.0 / np.sqrt(D), *key, 2),
+        "w_out": inputs.normal_bf16((D, D + F), 1.0 / np.sqrt(D + F), *key, 3),
+        "q_scale": inputs.f64_to_bf16_bits(np.ones(d)),
+        "k_scale": inputs.f64_to_bf16_bits(np.ones(d)),
+    }
+
+
+def stack_inputs(n_img_side, n_txt, n_i, n_t, n_j, seed=0, zero_gate=False):
+    n_img = n_img_side * n_img_side
+    cfg = configs.BlockConfig("stack", 99, (configs.Stream("image", n_img, (n_img_side, n_img_side), 0.7),
+                                            configs.Stream("text", n_txt)))
+    pos = inputs.positions(cfg)
+    x_img = inputs.normal_bf16((n_img, D), 1.0, seed, 401)
+    x_c = inputs.normal_bf16((n_txt, D), 1.0, seed, 402)
+    x_n = inputs.normal_bf16((n_txt, D), 1.0, seed, 403)
+    blocks = ([block_params(seed, i, 1, zero_gate) for i in range(n_i)]
+              + [block_params(seed, 10 + i, 1, zero_gate) for i in range(n_t)]
+              + [block_params(seed, 20 + i, 2, zero_gate) for i in range(n_j)])
+    return x_img, x_c, x_n, pos, blocks
+
+
+def to_dev_blocks(blocks):
+    return [{k: ops.to_device_bf16(v) for k, v in b.items()} for b in blocks]
+
+
+def run_stack(x_img, x_c, x_n, pos, blocks, n_i, n_t, n_j, scale):
+    desc = ops.make_stack_desc(x_img.shape[0], x_c.shape[0], n_i, n_t, n_j, scale)
+    v = ops.stack_fwd(desc, ops.to_device_bf16(x_img), ops.to_device_bf16(x_c),
+                      None if x_n is None else ops.to_device_bf16(x_n),
+                      torch.from_numpy(pos).cuda(), to_dev_blocks(blocks))
+    torch.cuda.synchronize()
+    return widen(v)
+
+
+@pytest.mark.parametrize("scale", [4.0, 1.0])
+def test_stack_cfg_parity(scale):
+    require_gpu()
+    n_i, n_t, n_j = 1, 1, 2
+    x_img, x_c, x_n, pos, blocks = stack_inputs(16, 80, n_i, n_t, n_j)
+    log(f"stack 256 img + 80 txt, blocks {n_i}+{n_t}+{n_j}, cfg {scale}")
+    got = run_stack(x_img, x_c, x_n if scale != 1.0 else None, pos, blocks, n_i, n_t, n_j, scale)
+    want = oracle.stack_cfg_ref(x_img, x_c, x_n, pos, blocks[:n_i], blocks[n_i:n_i + n_t],
+                                blocks[n_i + n_t:], DIMS, scale)
+    e = oracle.rel_l2(got, want)
+    log(f"  relL2 {e:.3e}")
+    assert e <= TOL_STACK
+
+
+def test_stack_zero_gates_return_the_image_tokens():
+    require_gpu()
+    x_img, x_c, x_n, pos, blocks = stack_inputs(8, 40, 1, 1, 1, seed=3, zero_gate=True)
+    got = run_stack(x_img, x_c, x_n, pos, blocks, 1, 1, 1, 4.0)
+    assert np.array_equal(got, oracle.widen_bf16(x_img))
+
+
+def test_stack_identical_prompts_give_the_conditional_branch():
+    require_gpu()
+    x_img, x_c, _, pos, blocks = stack_inputs(8, 40, 1, 1, 1, seed=4)
+    a = run_stack(x_img, x_c, x_c, pos, blocks, 1, 1, 1, 4.0)
+    b = run_stack(x_img, x_c, None, pos, blocks, 1, 1, 1, 1.0)
+    # neg == cond bitwise, so neg + 4 (cond - neg) == cond exactly
+    assert np.array_equal(a, b)

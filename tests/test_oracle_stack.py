@@ -42,7 +42,8 @@ def test_round_bf16_ties_to_even_and_idempotent():
     # 1 + 3 ulp/2 is a tie between 1 + ulp (odd) and 1 + 2 ulp (even)
     assert oracle.round_bf16(np.array([one + 1.5 * ulp]))[0] == one + 2 * ulp
     bits = np.arange(0, 1 << 16, 7, dtype=np.uint16)
-    vals = oracle.widen_bf16(bits)
+    with np.errstate(invalid="ignore"):  # the NaN patterns among them
+        vals = oracle.widen_bf16(bits)
     vals = vals[np.isfinite(vals)]
     assert np.array_equal(oracle.round_bf16(vals), vals)
 

@@ -10,7 +10,9 @@ steps gives per-stage times from HIP events the library records on the work
 stream between its kernels.  The fp64 CPU oracle of the same block
 is timed once on the host as a baseline and its output gives the parity of
 the timed configuration.  A secondary field times one guided denoise step of
-the two-stage stack (c5) through dit_stack_fwd (`--no-stack` skips it).
+the two-stage stack (c5) through dit_stack_fwd (`--no-stack` skips it), and
+another one block of the long 2048^2 editing sequence (2048^2 image, one
+2048^2 reference, 160 text tokens; `--no-long` skips it).
 
 Prints one JSON line.
 """
@@ -42,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the secondary measurement of the two-stage stack with CFG (c5)")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the secondary measurement of the long editing sequence")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the timed steps "
                          "(reference point for the profiler's FETCH_SIZE / WRITE_SIZE)")
@@ -146,6 +150,62 @@ def stack_c5(torch, configs, ops, steps: int, warmup: int) -> dict:
         "tflops_executed": round(flop_exec / (ms * 1e-3) / 1e12, 2),
         "gflop_executed": round(flop_exec / 1e9, 1),
         "gflop_two_full_forwards": round(flop_nominal / 1e9, 1),
+        "steps": steps, "warmup": warmup,
+    }
+
+
+def block_long(torch, configs, ops, timing, steps: int, warmup: int) -> dict:
+    """One block forward of the long editing sequence (N = 32,928) with
+    device-generated random weights, timed per stage with HIP events."""
+    cfg = configs.EDIT_2048
+    D, F, d = cfg.width, cfg.mlp_hidden, cfg.head_dim
+    from flow_matching_diffusion_adaln_amd import inputs
+    gen = torch.Generator(device="cuda").manual_seed(777)
+
+    def rnd(shape, std):
+        return (torch.randn(shape, generator=gen, device="cuda") * std).to(torch.bfloat16)
+
+    x = rnd((cfg.N, D), 1.0)
+    mod = rnd((cfg.n_streams, 3, D), 0.1 ** 0.5)
+    w_in, w_out = rnd((3 * D + 2 * F, D), D ** -0.5), rnd((D, D + F), (D + F) ** -0.5)
+    ones = torch.ones(d, dtype=torch.bfloat16, device="cuda")
+    pos = torch.from_numpy(inputs.positions(cfg)).cuda()
+    desc = ops.make_desc(cfg.n_tokens)
+    ws = ops.alloc_workspace(desc)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        ops.block_fwd(x, mod, pos, w_in, w_out, ones, ones, desc, y=y, workspace=ws,
+                      stream=stream, events=events)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [timing.create(ops.N_STAGES + 1) for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    st = {name: float(np.mean([timing.elapsed_ms(e[j], e[j + 1]) for e in evs]))
+          for j, name in enumerate(ops.STAGES)}
+    for e in evs:
+        timing.destroy(e)
+    assert bool(torch.isfinite(y.float()).all())
+    attn_tflops = cfg.attn_flop() / (st["attn"] * 1e-3) / 1e12
+    return {
+        "workload": f"{cfg.name}: {cfg.description}; one parallel block forward",
+        "ms_per_block": round(ms, 3),
+        "tflops": round(cfg.flop() / (ms * 1e-3) / 1e12, 2),
+        "gflop_per_block": round(cfg.flop() / 1e9, 1),
+        "attn_share_of_flop": round(cfg.attn_flop() / cfg.flop(), 3),
+        "stage_ms_mean": {k: round(v, 3) for k, v in st.items()},
+        "attn_tflops": round(attn_tflops, 2),
+        "attn_frac_mfma_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "steps": steps, "warmup": warmup,
     }
 
@@ -292,6 +352,8 @@ def main():
 
     if not args.no_stack:
         result["stack_c5"] = stack_c5(torch, configs, ops, steps=3, warmup=1)
+    if not args.no_long:
+        result["block_edit2048"] = block_long(torch, configs, ops, timing, steps=5, warmup=1)
 
     if not args.no_cpu_baseline:
         ref, sec, threads, blas = cpu_baseline(d, cfg)

@@ -110,7 +110,14 @@ C4 = BlockConfig(
     "c4", 5, (_img(64, 0.5), _ref(64), _txt(160)),
     description="1024^2 with one 1024^2 reference: 4096 + 4096 (l=1) + 160 text, N=8352")
 
-CONFIGS = {c.name: c for c in (C1, C2, C3_IMG, C3_TXT, C4)}
+# Long editing sequence: a 2048^2 image (a 128 x 128 latent grid) with one
+# 2048^2 reference and 160 text tokens, N = 32,928; attention is about 60% of
+# its FLOPs.
+EDIT_2048 = BlockConfig(
+    "edit2048", 6, (_img(128, 0.5), _ref(128), _txt(160)),
+    description="2048^2 edit: 16384 image + 16384 reference (l=1) + 160 text, N=32928")
+
+CONFIGS = {c.name: c for c in (C1, C2, C3_IMG, C3_TXT, C4, EDIT_2048)}
 
 
 @dataclass(frozen=True)

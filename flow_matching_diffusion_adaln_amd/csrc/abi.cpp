@@ -148,12 +148,15 @@ int block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const 
 }
 
 // Block descriptor of one stage of the stack: 1 stream of n tokens, or the
-// joint [image | text] pair.
-dit_block_desc stack_block_desc(const dit_stack_desc* d, int n_streams, int n0, int n1) {
+// joint [image | reference | text] sequence (the reference segment only when
+// there are reference tokens).
+dit_block_desc stack_block_desc(const dit_stack_desc* d, int n_streams, int n0, int n1 = 0,
+                                int n2 = 0) {
   dit_block_desc b{};
   b.n_streams = n_streams;
   b.n_tokens[0] = n0;
   b.n_tokens[1] = n1;
+  b.n_tokens[2] = n2;
   b.width = d->width;
   b.n_heads = d->n_heads;
   b.head_dim = d->head_dim;
@@ -165,19 +168,26 @@ dit_block_desc stack_block_desc(const dit_stack_desc* d, int n_streams, int n0, 
   return b;
 }
 
+dit_block_desc joint_desc(const dit_stack_desc* d) {
+  return d->n_ref > 0 ? stack_block_desc(d, 3, d->n_img, d->n_ref, d->n_txt)
+                      : stack_block_desc(d, 2, d->n_img, d->n_txt);
+}
+
 constexpr int kMaxStackBlocks = 1024;
 
 // Validates the stack descriptor; on success `joint` is the joint block's
 // shape and *bytes the workspace the stack needs.
 int check_stack(const dit_stack_desc* d, Shape* joint, size_t* bytes) {
   if (!d) return DIT_ERR_NULL;
-  if (d->n_img <= 0 || d->n_txt <= 0 || d->n_img_blocks < 0 || d->n_txt_blocks < 0 ||
-      d->n_joint_blocks < 0)
+  if (d->n_img <= 0 || d->n_ref < 0 || d->n_txt <= 0 || d->n_img_blocks < 0 ||
+      d->n_ref_blocks < 0 || d->n_txt_blocks < 0 || d->n_joint_blocks < 0)
     return DIT_ERR_SHAPE;
-  if ((long long)d->n_img_blocks + d->n_txt_blocks + d->n_joint_blocks > kMaxStackBlocks)
+  if (d->n_ref == 0 && d->n_ref_blocks != 0) return DIT_ERR_SHAPE;
+  if ((long long)d->n_img_blocks + d->n_ref_blocks + d->n_txt_blocks + d->n_joint_blocks >
+      kMaxStackBlocks)
     return DIT_ERR_SHAPE;
   if (!isfinite(d->cfg_scale)) return DIT_ERR_ARG;
-  const dit_block_desc jd = stack_block_desc(d, 2, d->n_img, d->n_txt);
+  const dit_block_desc jd = joint_desc(d);
   const int rc = check_desc(&jd, joint);
   if (rc != DIT_OK) return rc;
   const size_t act = round_up((size_t)joint->N * joint->D * 2);
@@ -298,27 +308,33 @@ int dit_stack_workspace_bytes(const dit_stack_desc* desc, size_t* bytes) {
   return DIT_OK;
 }
 
-int dit_stack_fwd(const dit_stack_desc* desc, const void* x_img, const void* x_txt_cond,
-                  const void* x_txt_neg, const int32_t* pos, const dit_block_params* blocks,
-                  void* v_img, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int dit_stack_fwd(const dit_stack_desc* desc, const void* x_img, const void* x_ref,
+                  const void* x_txt_cond, const void* x_txt_neg, const int32_t* pos,
+                  const dit_block_params* blocks, void* v_img, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
   Shape js;
   size_t need = 0;
   int rc = check_stack(desc, &js, &need);
   if (rc != DIT_OK) return rc;
   const bool guided = desc->cfg_scale != 1.0f;
-  const int n_blocks = desc->n_img_blocks + desc->n_txt_blocks + desc->n_joint_blocks;
-  if (!x_img || !x_txt_cond || (guided && !x_txt_neg) || !pos || !v_img || !workspace ||
-      (n_blocks > 0 && !blocks))
+  const bool refs = desc->n_ref > 0;
+  const int n_blocks =
+      desc->n_img_blocks + desc->n_ref_blocks + desc->n_txt_blocks + desc->n_joint_blocks;
+  if (!x_img || (refs && !x_ref) || !x_txt_cond || (guided && !x_txt_neg) || !pos || !v_img ||
+      !workspace || (n_blocks > 0 && !blocks))
     return DIT_ERR_NULL;
-  if (misaligned(x_img) || misaligned(x_txt_cond) || (guided && misaligned(x_txt_neg)) ||
-      misaligned(pos) || misaligned(v_img) || misaligned(workspace))
+  if (misaligned(x_img) || (refs && misaligned(x_ref)) || misaligned(x_txt_cond) ||
+      (guided && misaligned(x_txt_neg)) || misaligned(pos) || misaligned(v_img) ||
+      misaligned(workspace))
     return DIT_ERR_ALIGN;
   // every block is checked before anything is launched
   for (int i = 0; i < n_blocks; ++i)
     if ((rc = check_params(blocks[i])) != DIT_OK) return rc;
   if (workspace_bytes < need) return DIT_ERR_WORKSPACE;
   const size_t row = (size_t)js.D * 2;  // bytes per token row
-  const size_t img_bytes = (size_t)desc->n_img * row, txt_bytes = (size_t)desc->n_txt * row;
+  const size_t img_bytes = (size_t)desc->n_img * row, ref_bytes = (size_t)desc->n_ref * row,
+               txt_bytes = (size_t)desc->n_txt * row;
+  const size_t pre_bytes = img_bytes + ref_bytes;  // the rows both branches share
   if (overlaps(v_img, img_bytes, workspace, need)) return DIT_ERR_ARG;
 
   char* wsp = static_cast<char*>(workspace);
@@ -326,41 +342,48 @@ int dit_stack_fwd(const dit_stack_desc* desc, const void* x_img, const void* x_t
   const size_t act = round_up((size_t)js.N * row);
   char* xc = wsp + block_ws;        // [N, D] activations of the prompt branch
   char* xn = xc + act;              // [N, D] activations of the negative branch
-  const dit_block_desc di = stack_block_desc(desc, 1, desc->n_img, 0);
-  const dit_block_desc dt = stack_block_desc(desc, 1, desc->n_txt, 0);
-  const dit_block_desc dj = stack_block_desc(desc, 2, desc->n_img, desc->n_txt);
-  const int32_t* pos_txt = pos + (size_t)desc->n_img * 4;
+  const dit_block_desc di = stack_block_desc(desc, 1, desc->n_img);
+  const dit_block_desc dr = stack_block_desc(desc, 1, desc->n_ref);
+  const dit_block_desc dt = stack_block_desc(desc, 1, desc->n_txt);
+  const dit_block_desc dj = joint_desc(desc);
+  const int32_t* pos_ref = pos + (size_t)desc->n_img * 4;
+  const int32_t* pos_txt = pos_ref + (size_t)desc->n_ref * 4;
   const dit_block_params* bi = blocks;
-  const dit_block_params* bt = blocks + desc->n_img_blocks;
+  const dit_block_params* br = bi + desc->n_img_blocks;
+  const dit_block_params* bt = br + desc->n_ref_blocks;
   const dit_block_params* bj = bt + desc->n_txt_blocks;
   auto run = [&](const dit_block_desc& d, const dit_block_params& p, char* h,
                  const int32_t* ps) -> int {
     return block_fwd(&d, h, p.mod, ps, p.w_in, p.w_out, p.q_scale, p.k_scale, h, wsp, block_ws,
                      stream, nullptr);
   };
+  auto copy = [&](void* dst, const void* src, size_t n) -> int {
+    return hip_status(hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, stream));
+  };
 
-  // stage 1, image: shared by both branches
-  if ((rc = hip_status(hipMemcpyAsync(xc, x_img, img_bytes, hipMemcpyDeviceToDevice, stream))))
-    return rc;
+  // stage 1, image and reference: shared by both branches
+  if ((rc = copy(xc, x_img, img_bytes)) != DIT_OK) return rc;
   for (int i = 0; i < desc->n_img_blocks; ++i)
     if ((rc = run(di, bi[i], xc, pos)) != DIT_OK) return rc;
-  if (guided &&
-      (rc = hip_status(hipMemcpyAsync(xn, xc, img_bytes, hipMemcpyDeviceToDevice, stream))))
-    return rc;
-  // stage 1, text, then the joint blocks, per branch (in place on [image | text])
+  if (refs) {
+    if ((rc = copy(xc + img_bytes, x_ref, ref_bytes)) != DIT_OK) return rc;
+    for (int i = 0; i < desc->n_ref_blocks; ++i)
+      if ((rc = run(dr, br[i], xc + img_bytes, pos_ref)) != DIT_OK) return rc;
+  }
+  if (guided && (rc = copy(xn, xc, pre_bytes)) != DIT_OK) return rc;
+  // stage 1, text, then the joint blocks, per branch (in place on
+  // [image | reference | text])
   auto branch = [&](char* h, const void* x_txt) -> int {
-    int r = hip_status(hipMemcpyAsync(h + img_bytes, x_txt, txt_bytes, hipMemcpyDeviceToDevice,
-                                      stream));
+    int r = copy(h + pre_bytes, x_txt, txt_bytes);
     if (r != DIT_OK) return r;
     for (int i = 0; i < desc->n_txt_blocks; ++i)
-      if ((r = run(dt, bt[i], h + img_bytes, pos_txt)) != DIT_OK) return r;
+      if ((r = run(dt, bt[i], h + pre_bytes, pos_txt)) != DIT_OK) return r;
     for (int i = 0; i < desc->n_joint_blocks; ++i)
       if ((r = run(dj, bj[i], h, pos)) != DIT_OK) return r;
     return DIT_OK;
   };
   if ((rc = branch(xc, x_txt_cond)) != DIT_OK) return rc;
-  if (!guided)
-    return hip_status(hipMemcpyAsync(v_img, xc, img_bytes, hipMemcpyDeviceToDevice, stream));
+  if (!guided) return copy(v_img, xc, img_bytes);
   if ((rc = branch(xn, x_txt_neg)) != DIT_OK) return rc;
   return hip_status(dit::launch_cfg_combine(reinterpret_cast<const uint16_t*>(xc),
                                             reinterpret_cast<const uint16_t*>(xn),

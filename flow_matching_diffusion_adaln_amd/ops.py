@@ -45,8 +45,10 @@ class BlockDesc(ctypes.Structure):
 class StackDesc(ctypes.Structure):
     _fields_ = [
         ("n_img", ctypes.c_int32),
+        ("n_ref", ctypes.c_int32),
         ("n_txt", ctypes.c_int32),
         ("n_img_blocks", ctypes.c_int32),
+        ("n_ref_blocks", ctypes.c_int32),
         ("n_txt_blocks", ctypes.c_int32),
         ("n_joint_blocks", ctypes.c_int32),
         ("width", ctypes.c_int32),
@@ -85,7 +87,7 @@ def load_library() -> ctypes.CDLL:
     lib.adaln_mod.argtypes = [i32, ctypes.POINTER(i32), i32, vp, vp, vp, f32, vp]
     stack_p = ctypes.POINTER(StackDesc)
     lib.dit_stack_workspace_bytes.argtypes = [stack_p, ctypes.POINTER(sz)]
-    lib.dit_stack_fwd.argtypes = [stack_p, vp, vp, vp, vp, ctypes.POINTER(BlockParams), vp, vp,
+    lib.dit_stack_fwd.argtypes = [stack_p, vp, vp, vp, vp, vp, ctypes.POINTER(BlockParams), vp, vp,
                                   sz, vp]
     lib.dit_status_str.argtypes = [ctypes.c_int]
     lib.dit_status_str.restype = ctypes.c_char_p
@@ -246,12 +248,14 @@ def to_host_bits(t: torch.Tensor):
 
 
 def make_stack_desc(n_img: int, n_txt: int, n_img_blocks: int, n_txt_blocks: int,
-                    n_joint_blocks: int, cfg_scale: float, width: int = configs.WIDTH,
-                    n_heads: int = configs.N_HEADS, head_dim: int = configs.HEAD_DIM,
+                    n_joint_blocks: int, cfg_scale: float, n_ref: int = 0, n_ref_blocks: int = 0,
+                    width: int = configs.WIDTH, n_heads: int = configs.N_HEADS,
+                    head_dim: int = configs.HEAD_DIM,
                     mlp_hidden: int = configs.MLP_HIDDEN) -> StackDesc:
     d = StackDesc()
-    d.n_img, d.n_txt = n_img, n_txt
-    d.n_img_blocks, d.n_txt_blocks, d.n_joint_blocks = n_img_blocks, n_txt_blocks, n_joint_blocks
+    d.n_img, d.n_ref, d.n_txt = n_img, n_ref, n_txt
+    d.n_img_blocks, d.n_ref_blocks = n_img_blocks, n_ref_blocks
+    d.n_txt_blocks, d.n_joint_blocks = n_txt_blocks, n_joint_blocks
     d.width, d.n_heads, d.head_dim, d.mlp_hidden = width, n_heads, head_dim, mlp_hidden
     d.rope_theta, d.ln_eps, d.qk_eps = configs.ROPE_THETA, configs.LN_EPS, configs.QK_EPS
     d.cfg_scale = cfg_scale
@@ -265,24 +269,31 @@ def stack_workspace_bytes(desc: StackDesc) -> int:
 
 
 def stack_fwd(desc: StackDesc, x_img, x_txt_cond, x_txt_neg, pos, blocks, v_img=None,
-              workspace=None, stream=None) -> torch.Tensor:
+              workspace=None, stream=None, x_ref=None) -> torch.Tensor:
     """v_img = dit_stack_fwd(...).  blocks: sequence of dicts with keys mod,
-    w_in, w_out, q_scale, k_scale (image blocks, then text, then joint)."""
+    w_in, w_out, q_scale, k_scale (image blocks, then reference, text and
+    joint blocks); x_ref is required when desc.n_ref > 0."""
     D, F, d = desc.width, desc.mlp_hidden, desc.head_dim
-    N = desc.n_img + desc.n_txt
+    N = desc.n_img + desc.n_ref + desc.n_txt
     _bf16(x_img, (desc.n_img, D), "x_img")
+    if desc.n_ref > 0:
+        if x_ref is None:
+            raise ValueError("x_ref is required when n_ref > 0")
+        _bf16(x_ref, (desc.n_ref, D), "x_ref")
     _bf16(x_txt_cond, (desc.n_txt, D), "x_txt_cond")
     if x_txt_neg is not None:
         _bf16(x_txt_neg, (desc.n_txt, D), "x_txt_neg")
     if pos.dtype != torch.int32 or tuple(pos.shape) != (N, 4) or not pos.is_cuda \
             or not pos.is_contiguous():
-        raise ValueError("pos must be a contiguous int32 [n_img + n_txt, 4] GPU tensor")
-    n_blocks = desc.n_img_blocks + desc.n_txt_blocks + desc.n_joint_blocks
+        raise ValueError("pos must be a contiguous int32 [n_img + n_ref + n_txt, 4] GPU tensor")
+    n_stage1 = desc.n_img_blocks + desc.n_ref_blocks + desc.n_txt_blocks
+    n_blocks = n_stage1 + desc.n_joint_blocks
     if len(blocks) != n_blocks:
         raise ValueError(f"expected {n_blocks} blocks, got {len(blocks)}")
+    s_joint = 3 if desc.n_ref > 0 else 2
     arr = (BlockParams * max(n_blocks, 1))()
     for i, b in enumerate(blocks):
-        s = 1 if i < desc.n_img_blocks + desc.n_txt_blocks else 2
+        s = 1 if i < n_stage1 else s_joint
         _bf16(b["mod"], (s, 3, D), f"blocks[{i}].mod")
         _bf16(b["w_in"], (3 * D + 2 * F, D), f"blocks[{i}].w_in")
         _bf16(b["w_out"], (D, D + F), f"blocks[{i}].w_out")
@@ -297,7 +308,7 @@ def stack_fwd(desc: StackDesc, x_img, x_txt_cond, x_txt_neg, pos, blocks, v_img=
         workspace = torch.empty(stack_workspace_bytes(desc), dtype=torch.uint8,
                                 device=x_img.device)
     _check(load_library().dit_stack_fwd(
-        ctypes.byref(desc), _ptr(x_img), _ptr(x_txt_cond), _ptr(x_txt_neg),
+        ctypes.byref(desc), _ptr(x_img), _ptr(x_ref), _ptr(x_txt_cond), _ptr(x_txt_neg),
         ctypes.c_void_p(pos.data_ptr()), arr, _ptr(v_img), _ptr(workspace),
         ctypes.c_size_t(workspace.numel()), _stream(stream)))
     return v_img

@@ -153,20 +153,26 @@ int adaln_mod(int32_t n_streams, const int32_t* n_tokens, int32_t width, const v
 
 /* ---- Two-stage stack and classifier-free guidance -------------------------
  * One denoise step of the transformer ("Welcome FLUX.3 Image Klein in
- * Diffusers", section "How it works": each stream first runs through blocks of
- * its own, attending only to itself, then the streams are concatenated and
- * run through the shared joint blocks; the miles page "FLUX 3 Image Klein",
- * section 3: the guided prediction is neg + scale * (pos - neg) from a forward
- * with the prompt and one with the negative prompt).  Every block is the
- * parallel block of dit_block_fwd.  Embedders and output layers are not part
- * of this call: image and text tokens enter as given, and the guided result
- * is taken on the image rows of the joint stack's output. */
+ * Diffusers", section "How it works": each stream, text, image and
+ * reference, first runs through blocks of its own, attending only to itself,
+ * then the streams are concatenated and run through the shared joint blocks;
+ * the miles page "FLUX 3 Image Klein", section 3: the guided prediction is
+ * neg + scale * (pos - neg) from a forward with the prompt and one with the
+ * negative prompt).  Every block is the parallel block of dit_block_fwd.
+ * Embedders and output layers are not part of this call: the tokens enter as
+ * given, and the guided result is taken on the image rows of the joint
+ * stack's output.  All reference images form one reference stream (their
+ * rows carry their own l index in pos), which runs the reference blocks as
+ * one sequence. */
 typedef struct dit_stack_desc {
   int32_t n_img;          /* image tokens (> 0)                                    */
+  int32_t n_ref;          /* reference tokens, all references together (>= 0)     */
   int32_t n_txt;          /* text tokens of each branch (> 0)                      */
   int32_t n_img_blocks;   /* stage-1 image blocks (5)                              */
+  int32_t n_ref_blocks;   /* stage-1 reference blocks (5; 0 when n_ref == 0)       */
   int32_t n_txt_blocks;   /* stage-1 text blocks (5)                               */
-  int32_t n_joint_blocks; /* stage-2 joint blocks over [image | text] (28)         */
+  int32_t n_joint_blocks; /* stage-2 joint blocks over [image | reference | text]  */
+                          /* (28)                                                  */
   int32_t width;          /* D, 3072                                               */
   int32_t n_heads;        /* H, 24                                                 */
   int32_t head_dim;       /* 128                                                   */
@@ -180,7 +186,9 @@ typedef struct dit_stack_desc {
 
 /* Device pointers of one block's parameters. */
 typedef struct dit_block_params {
-  const void* mod;     /* bf16 [S, 3, D]: S = 1 for a stage-1 block, 2 (image, text) for a joint block */
+  const void* mod;     /* bf16 [S, 3, D]: S = 1 for a stage-1 block; for a joint  */
+                       /* block S = 3 (image, reference, text) when n_ref > 0,    */
+                       /* else 2 (image, text)                                    */
   const void* w_in;    /* bf16 [3D + 2F, D], as in dit_block_fwd */
   const void* w_out;   /* bf16 [D, D + F]  */
   const void* q_scale; /* bf16 [d]         */
@@ -188,26 +196,33 @@ typedef struct dit_block_params {
 } dit_block_params;
 
 /* Bytes of device workspace dit_stack_fwd needs: the block workspace at
- * N = n_img + n_txt plus two [N, D] bf16 activation buffers (one per branch). */
+ * N = n_img + n_ref + n_txt plus two [N, D] bf16 activation buffers (one per
+ * branch). */
 int dit_stack_workspace_bytes(const dit_stack_desc* desc, size_t* bytes);
 
 /* One guided stack forward.
  *   x_img       bf16 [n_img, D]   image tokens entering stage 1
+ *   x_ref       bf16 [n_ref, D]   reference tokens (null when n_ref == 0)
  *   x_txt_cond  bf16 [n_txt, D]   text tokens of the prompt
  *   x_txt_neg   bf16 [n_txt, D]   text tokens of the negative prompt (may be
  *                                 null when cfg_scale == 1)
- *   pos         int32 [n_img + n_txt, 4]  joint (t, h, w, l) positions, image
- *                                 rows first; stage-1 blocks use their rows
- *   blocks      host array of n_img_blocks + n_txt_blocks + n_joint_blocks
- *               entries: image blocks, then text blocks, then joint blocks
+ *   pos         int32 [n_img + n_ref + n_txt, 4]  joint (t, h, w, l) positions
+ *                                 in [image | reference | text] order;
+ *                                 stage-1 blocks use their rows
+ *   blocks      host array of n_img_blocks + n_ref_blocks + n_txt_blocks +
+ *               n_joint_blocks entries in that order
  *   v_img       bf16 [n_img, D]   out: neg + cfg_scale * (cond - neg) on the
  *                                 image rows of the joint output, in fp32, rounded
  *                                 to bf16 (the cond rows when cfg_scale == 1)
- * The stage-1 image blocks do not see the text, so both branches share them.
- * Activations between blocks are bf16, as in dit_block_fwd. */
-int dit_stack_fwd(const dit_stack_desc* desc, const void* x_img, const void* x_txt_cond,
-                  const void* x_txt_neg, const int32_t* pos, const dit_block_params* blocks,
-                  void* v_img, void* workspace, size_t workspace_bytes, hipStream_t stream);
+ * The stage-1 image and reference blocks do not see the text, so both
+ * branches share them.  Activations between blocks are bf16, as in
+ * dit_block_fwd.  Inputs are only read; v_img must not overlap the
+ * workspace.  Every size and block pointer is checked before the first
+ * launch; errors as for dit_block_fwd. */
+int dit_stack_fwd(const dit_stack_desc* desc, const void* x_img, const void* x_ref,
+                  const void* x_txt_cond, const void* x_txt_neg, const int32_t* pos,
+                  const dit_block_params* blocks, void* v_img, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
 
 /* Static name of a status code ("DIT_OK", "DIT_ERR_SHAPE: ...", ...). */
 const char* dit_status_str(int status);

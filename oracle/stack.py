@@ -8,8 +8,8 @@ What is computed (sources are the pages' sections):
 * Two-stage transformer: "Welcome FLUX.3 Image Klein in Diffusers", section
   "How it works": each stream (text, image, reference) first runs through
   blocks of its own (own weights, attending only to itself), then the streams
-  are concatenated and run through the shared joint blocks (5 own blocks per
-  stream, then 28 joint blocks).
+  are concatenated in [image | reference | text] order and run through the
+  shared joint blocks (5 own blocks per stream, then 28 joint blocks).
 * Classifier-free guidance: the miles page "FLUX 3 Image Klein", section 3
   "Family config": the guided prediction is neg + scale * (pos - neg), from
   one forward with the prompt and one with the negative prompt; a scale of 1
@@ -21,8 +21,10 @@ Readings taken where the pages are silent:
   output (the output layers, also out of scope, act on image tokens only);
   activations are bf16 between blocks (the model runs in bf16), rounded to
   nearest even; the stage-1 image blocks do not depend on the text, so both
-  branches share them; stage-1 blocks use the image rows' (resp. text rows')
-  positions of the joint sequence.
+  branches share them, as they share the reference blocks; stage-1 blocks use
+  their own rows of the joint sequence's position table; all reference images
+  together form the one reference stream (each keeps its own l index in the
+  positions) and run the reference blocks as one sequence.
 """
 from __future__ import annotations
 
@@ -68,28 +70,48 @@ def _run(h: np.ndarray, blocks: Sequence[Dict], pos: np.ndarray, n_tokens: Seque
     return h
 
 
+def _bits_or_float(a) -> np.ndarray:
+    a = np.asarray(a)
+    return widen_bf16(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
 def stack_branch(x_img, x_txt, pos, img_blocks: List[Dict], txt_blocks: List[Dict],
-                 joint_blocks: List[Dict], dims: Dict) -> np.ndarray:
+                 joint_blocks: List[Dict], dims: Dict, x_ref=None,
+                 ref_blocks: Sequence[Dict] = ()) -> np.ndarray:
     """One forward of the two-stage stack: stage-1 image blocks on the image
-    rows, stage-1 text blocks on the text rows, then the joint blocks over
-    [image | text].  Returns the joint output [n_img + n_txt, D] (bf16 values)."""
-    x_img = widen_bf16(x_img) if np.asarray(x_img).dtype == np.uint16 else np.asarray(x_img, np.float64)
-    x_txt = widen_bf16(x_txt) if np.asarray(x_txt).dtype == np.uint16 else np.asarray(x_txt, np.float64)
+    rows, stage-1 reference blocks on the reference rows (when there are
+    references), stage-1 text blocks on the text rows, then the joint blocks
+    over [image | reference | text].  Returns the joint output [N, D] (bf16
+    values)."""
+    x_img, x_txt = _bits_or_float(x_img), _bits_or_float(x_txt)
     pos = np.asarray(pos, dtype=np.int64)
     n_img, n_txt = x_img.shape[0], x_txt.shape[0]
-    h_img = _run(x_img, img_blocks, pos[:n_img], [n_img], dims)
-    h_txt = _run(x_txt, txt_blocks, pos[n_img:], [n_txt], dims)
-    h = np.concatenate([h_img, h_txt], axis=0)
-    return _run(h, joint_blocks, pos, [n_img, n_txt], dims)
+    parts, n_tokens = [_run(x_img, img_blocks, pos[:n_img], [n_img], dims)], [n_img]
+    if x_ref is not None and np.asarray(x_ref).shape[0] > 0:
+        x_ref = _bits_or_float(x_ref)
+        n_ref = x_ref.shape[0]
+        parts.append(_run(x_ref, ref_blocks, pos[n_img:n_img + n_ref], [n_ref], dims))
+        n_tokens.append(n_ref)
+    elif len(ref_blocks):
+        raise ValueError("reference blocks without reference tokens")
+    n_pre = sum(n_tokens)
+    parts.append(_run(x_txt, txt_blocks, pos[n_pre:], [n_txt], dims))
+    n_tokens.append(n_txt)
+    if pos.shape[0] != n_pre + n_txt:
+        raise ValueError("pos does not cover [image | reference | text]")
+    return _run(np.concatenate(parts, axis=0), joint_blocks, pos, n_tokens, dims)
 
 
 def stack_cfg_ref(x_img, x_txt_cond, x_txt_neg, pos, img_blocks, txt_blocks, joint_blocks,
-                  dims: Dict, cfg_scale: float) -> np.ndarray:
+                  dims: Dict, cfg_scale: float, x_ref=None, ref_blocks: Sequence[Dict] = ()
+                  ) -> np.ndarray:
     """Guided image rows neg + s (cond - neg) of two stack forwards, rounded to
     bf16 like the GPU output.  cfg_scale == 1 runs the conditional branch only."""
     n_img = np.asarray(x_img).shape[0]
-    cond = stack_branch(x_img, x_txt_cond, pos, img_blocks, txt_blocks, joint_blocks, dims)
+    cond = stack_branch(x_img, x_txt_cond, pos, img_blocks, txt_blocks, joint_blocks, dims,
+                        x_ref, ref_blocks)
     if cfg_scale == 1.0:
         return cond[:n_img]
-    neg = stack_branch(x_img, x_txt_neg, pos, img_blocks, txt_blocks, joint_blocks, dims)
+    neg = stack_branch(x_img, x_txt_neg, pos, img_blocks, txt_blocks, joint_blocks, dims,
+                       x_ref, ref_blocks)
     return round_bf16(cfg_combine(cond[:n_img], neg[:n_img], cfg_scale))

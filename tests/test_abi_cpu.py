@@ -187,7 +187,7 @@ def stack_ws(lib, d):
 
 
 def test_stack_struct_layout():
-    assert ctypes.sizeof(ops.StackDesc) == 52
+    assert ctypes.sizeof(ops.StackDesc) == 60
     assert ctypes.sizeof(ops.BlockParams) == 40
 
 
@@ -199,12 +199,19 @@ def test_stack_workspace_bytes(lib):
     # the block workspace at N = 4256 plus one [N, D] bf16 buffer per branch
     assert n == nb + 2 * 4256 * 3072 * 2
     assert lib.dit_stack_workspace_bytes(None, ctypes.byref(ctypes.c_size_t())) == NULL
+    # with 4096 reference tokens the joint sequence is [image | reference | text]
+    rc, n = stack_ws(lib, ops.make_stack_desc(4096, 160, 5, 5, 28, 4.0, n_ref=4096,
+                                              n_ref_blocks=5))
+    rc_b, nb = ws(lib, ops.make_desc([4096, 4096, 160]))
+    assert rc == OK and n == nb + 2 * 8352 * 3072 * 2
 
 
 @pytest.mark.parametrize("field,value,want", [
     ("n_img", 0, SHAPE), ("n_txt", 0, SHAPE), ("n_img_blocks", -1, SHAPE),
     ("n_joint_blocks", 2000, SHAPE), ("width", 3000, SHAPE), ("head_dim", 64, SHAPE),
-    ("cfg_scale", float("nan"), ARG), ("qk_eps", -1.0, ARG)])
+    ("cfg_scale", float("nan"), ARG), ("qk_eps", -1.0, ARG), ("n_ref", -1, SHAPE),
+    ("n_ref_blocks", 1, SHAPE),  # reference blocks without reference tokens
+    ("n_ref", 131072, SHAPE)])  # the joint sequence above DIT_MAX_TOKENS
 def test_stack_desc_validation(lib, field, value, want):
     d = ops.make_stack_desc(256, 80, 1, 1, 2, 4.0)
     setattr(d, field, value)
@@ -212,8 +219,9 @@ def test_stack_desc_validation(lib, field, value, want):
 
 
 def stack_call(lib, d, x_img=P, x_c=P + (1 << 30), x_n=P + (2 << 30), pos=P + (3 << 30),
-               blocks="ok", v=P + (4 << 30), wsp=P + (5 << 30), ws_bytes=None):
-    n_blocks = d.n_img_blocks + d.n_txt_blocks + d.n_joint_blocks
+               blocks="ok", v=P + (4 << 30), wsp=P + (5 << 30), ws_bytes=None,
+               x_ref=P + (1 << 29)):
+    n_blocks = d.n_img_blocks + d.n_ref_blocks + d.n_txt_blocks + d.n_joint_blocks
     arr = (ops.BlockParams * max(n_blocks, 1))()
     for i in range(n_blocks):
         for j, name in enumerate(("mod", "w_in", "w_out", "q_scale", "k_scale")):
@@ -226,7 +234,8 @@ def stack_call(lib, d, x_img=P, x_c=P + (1 << 30), x_n=P + (2 << 30), pos=P + (3
         ws_bytes = stack_ws(lib, d)[1]
     c = ctypes.c_void_p
     return lib.dit_stack_fwd(ctypes.byref(d), c(x_img) if x_img else None,
-                             c(x_c) if x_c else None, c(x_n) if x_n else None,
+                             c(x_ref) if x_ref else None, c(x_c) if x_c else None,
+                             c(x_n) if x_n else None,
                              c(pos) if pos else None, None if blocks is None else arr,
                              c(v) if v else None, c(wsp) if wsp else None,
                              ctypes.c_size_t(ws_bytes), None)
@@ -243,3 +252,9 @@ def test_stack_fwd_host_errors(lib):
     assert stack_call(lib, d, x_c=BAD) == ALIGN
     assert stack_call(lib, d, ws_bytes=stack_ws(lib, d)[1] - 1) == WS
     assert stack_call(lib, d, v=P + (5 << 30)) == ARG      # output inside the workspace
+    # no references: a null x_ref passes the pointer checks (stopped here by the workspace)
+    assert stack_call(lib, d, x_ref=0, ws_bytes=stack_ws(lib, d)[1] - 1) == WS
+    r = ops.make_stack_desc(256, 80, 1, 1, 2, 4.0, n_ref=64, n_ref_blocks=1)
+    assert stack_call(lib, r, x_ref=0) == NULL
+    assert stack_call(lib, r, x_ref=BAD) == ALIGN
+    assert stack_call(lib, r, blocks="bad_null") == NULL

@@ -56,11 +56,14 @@ def to_dev_blocks(blocks):
     return [{k: ops.to_device_bf16(v) for k, v in b.items()} for b in blocks]
 
 
-def run_stack(x_img, x_c, x_n, pos, blocks, n_i, n_t, n_j, scale):
-    desc = ops.make_stack_desc(x_img.shape[0], x_c.shape[0], n_i, n_t, n_j, scale)
+def run_stack(x_img, x_c, x_n, pos, blocks, n_i, n_t, n_j, scale, x_ref=None, n_r=0):
+    n_ref = 0 if x_ref is None else x_ref.shape[0]
+    desc = ops.make_stack_desc(x_img.shape[0], x_c.shape[0], n_i, n_t, n_j, scale,
+                               n_ref=n_ref, n_ref_blocks=n_r)
     v = ops.stack_fwd(desc, ops.to_device_bf16(x_img), ops.to_device_bf16(x_c),
                       None if x_n is None else ops.to_device_bf16(x_n),
-                      torch.from_numpy(pos).cuda(), to_dev_blocks(blocks))
+                      torch.from_numpy(pos).cuda(), to_dev_blocks(blocks),
+                      x_ref=None if x_ref is None else ops.to_device_bf16(x_ref))
     torch.cuda.synchronize()
     return widen(v)
 
@@ -93,3 +96,25 @@ def test_stack_identical_prompts_give_the_conditional_branch():
     b = run_stack(x_img, x_c, None, pos, blocks, 1, 1, 1, 1.0)
     # neg == cond bitwise, so neg + 4 (cond - neg) == cond exactly
     assert np.array_equal(a, b)
+
+
+def test_stack_with_two_references_parity():
+    # 256 image tokens | two 8 x 8 references (l = 1, 2) | 80 text tokens;
+    # blocks: 1 image, 1 reference, 1 text, 2 joint (three-stream modulation)
+    require_gpu()
+    n_i, n_r, n_t, n_j = 1, 1, 1, 2
+    x_img, x_c, x_n, p, _ = stack_inputs(16, 80, 0, 0, 0, seed=6)
+    x_ref = inputs.normal_bf16((128, D), 1.0, 6, 404)
+    pr = np.zeros((128, 4), dtype=np.int32)
+    i = np.arange(128)
+    pr[:, 1], pr[:, 2], pr[:, 3] = (i % 64) // 8, i % 8, 1 + i // 64
+    pos = np.ascontiguousarray(np.concatenate([p[:256], pr, p[256:]]))
+    blocks = ([block_params(6, 0, 1)] + [block_params(6, 5, 1)] + [block_params(6, 10, 1)]
+              + [block_params(6, 20 + j, 3) for j in range(n_j)])
+    log("stack 256 img + 2x64 ref + 80 txt, blocks 1+1+1+2, cfg 4.0")
+    got = run_stack(x_img, x_c, x_n, pos, blocks, n_i, n_t, n_j, 4.0, x_ref=x_ref, n_r=n_r)
+    want = oracle.stack_cfg_ref(x_img, x_c, x_n, pos, blocks[:1], blocks[2:3], blocks[3:],
+                                DIMS, 4.0, x_ref=x_ref, ref_blocks=blocks[1:2])
+    e = oracle.rel_l2(got, want)
+    log(f"  relL2 {e:.3e}")
+    assert e <= TOL_STACK

@@ -138,3 +138,62 @@ def test_stage1_blocks_apply_per_stream_with_their_own_positions():
                           bt["k_scale"], [5], 2, 8, 24)["y"]
     assert np.array_equal(h[:12], oracle.round_bf16(yi))
     assert np.array_equal(h[12:], oracle.round_bf16(yt))
+
+
+def _ref_inputs(n_img=12, n_ref=8, n_txt=5, seed=0):
+    """Two references of 4 tokens each (2 x 2 grids, l = 1 and 2) between the
+    image and the text rows."""
+    x_img, x_c, x_n, p = _inputs(n_img, n_txt, seed)
+    x_ref = oracle.round_bf16(np.random.default_rng(seed + 100).standard_normal((n_ref, D)))
+    pr = np.zeros((n_ref, 4), dtype=np.int64)
+    i = np.arange(n_ref)
+    pr[:, 1], pr[:, 2], pr[:, 3] = (i % 4) // 2, i % 2, 1 + i // 4
+    pos = np.concatenate([p[:n_img], pr, p[n_img:]])
+    return x_img, x_ref, x_c, x_n, pos
+
+
+def test_reference_stage1_blocks_run_on_the_reference_rows():
+    x_img, x_ref, x_c, _, pos = _ref_inputs()
+    bi, br, bt = _block(51, 1), _block(52, 1), _block(53, 1)
+    h = oracle.stack_branch(x_img, x_c, pos, [bi], [bt], [], DIMS, x_ref=x_ref, ref_blocks=[br])
+    yr = oracle.block_ref(x_ref, br["mod"], pos[12:20], br["w_in"], br["w_out"], br["q_scale"],
+                          br["k_scale"], [8], 2, 8, 24)["y"]
+    yt = oracle.block_ref(x_c, bt["mod"], pos[20:], bt["w_in"], bt["w_out"], bt["q_scale"],
+                          bt["k_scale"], [5], 2, 8, 24)["y"]
+    assert h.shape == (25, D)
+    assert np.array_equal(h[12:20], oracle.round_bf16(yr))
+    assert np.array_equal(h[20:], oracle.round_bf16(yt))
+
+
+def test_joint_block_with_references_is_the_three_stream_block():
+    x_img, x_ref, x_c, _, pos = _ref_inputs()
+    b = _block(61, 3)
+    h = oracle.stack_branch(x_img, x_c, pos, [], [], [b], DIMS, x_ref=x_ref)
+    x = np.concatenate([x_img, x_ref, x_c])
+    y = oracle.block_ref(x, b["mod"], pos, b["w_in"], b["w_out"], b["q_scale"], b["k_scale"],
+                         [12, 8, 5], 2, 8, 24)["y"]
+    assert np.array_equal(h, oracle.round_bf16(y))
+
+
+def test_reference_stage_does_not_see_the_text_and_zero_gates_keep_the_image():
+    x_img, x_ref, x_c, x_n, pos = _ref_inputs()
+    br, bt = [_block(71, 1)], [_block(72, 1)]
+    a = oracle.stack_branch(x_img, x_c, pos, [], bt, [], DIMS, x_ref=x_ref, ref_blocks=br)
+    b = oracle.stack_branch(x_img, x_n, pos, [], bt, [], DIMS, x_ref=x_ref, ref_blocks=br)
+    assert np.array_equal(a[:20], b[:20])
+    zi, zr, zt = [_block(73, 1, True)], [_block(74, 1, True)], [_block(75, 1, True)]
+    out = oracle.stack_cfg_ref(x_img, x_c, x_n, pos, zi, zt, [_block(76, 3, True)], DIMS, 4.0,
+                               x_ref=x_ref, ref_blocks=zr)
+    assert np.array_equal(out, x_img)
+
+
+def test_the_reference_index_reaches_the_image_rows():
+    # the same reference tokens at l = 1, 2 or at l = 3, 4 give a different
+    # joint output on the image rows (RoPE's fourth axis is live)
+    x_img, x_ref, x_c, _, pos = _ref_inputs()
+    b = _block(81, 3)
+    a = oracle.stack_branch(x_img, x_c, pos, [], [], [b], DIMS, x_ref=x_ref)
+    pos2 = pos.copy()
+    pos2[12:20, 3] += 2
+    c = oracle.stack_branch(x_img, x_c, pos2, [], [], [b], DIMS, x_ref=x_ref)
+    assert not np.array_equal(a[:12], c[:12])

@@ -8,3 +8,6 @@ from .dit_block import (  # noqa: F401
     layer_norm, rel_l2, rope4_ref, rope_omega, silu, softmax_rows, stream_index, swiglu_ref,
     widen_bf16)
 from .stack import cfg_combine, round_bf16, stack_branch, stack_cfg_ref  # noqa: F401
+from .sampler import (  # noqa: F401
+    denoise_step, euler_cfg_step, flow_sigmas, linear, modulation, output_layers, sample,
+    sampler_prepare, time_embedding, timestep_sinusoid)

@@ -10,7 +10,8 @@ steps gives per-stage times from HIP events the library records on the work
 stream between its kernels.  The fp64 CPU oracle of the same block
 is timed once on the host as a baseline and its output gives the parity of
 the timed configuration.  A secondary field times one guided denoise step of
-the two-stage stack (c5) through dit_stack_fwd (`--no-stack` skips it), and
+the two-stage stack (c5) through dit_stack_fwd and the flow-matching sampler
+at the same shapes (`--no-stack` skips both), and
 another one block of the long 2048^2 editing sequence (2048^2 image, one
 2048^2 reference, 160 text tokens; `--no-long` skips it).
 
@@ -150,6 +151,85 @@ def stack_c5(torch, configs, ops, steps: int, warmup: int) -> dict:
         "tflops_executed": round(flop_exec / (ms * 1e-3) / 1e12, 2),
         "gflop_executed": round(flop_exec / 1e9, 1),
         "gflop_two_full_forwards": round(flop_nominal / 1e9, 1),
+        "steps": steps, "warmup": warmup,
+    }
+
+
+def sampler_c5(torch, configs, ops, steps: int, warmup: int) -> dict:
+    """The flow-matching sampler at c5 shapes (4,096 image + 160 text tokens,
+    5 + 5 stage-1 and 28 joint blocks, 128-channel latent, 20,480-wide text
+    features) with device-generated random weights: the step-invariant prepare,
+    guided steps (CFG 4) through dit_sampler_step, and one whole unguided
+    16-step generation (prepare + 16 steps)."""
+    sc = configs.C5
+    D, F, d = configs.WIDTH, configs.MLP_HIDDEN, configs.HEAD_DIM
+    C, T = 128, 20480
+    n_img, n_txt = sc.image_side * sc.image_side, sc.n_text
+    gen = torch.Generator(device="cuda").manual_seed(99)
+
+    def rnd(shape, std):
+        return (torch.randn(shape, generator=gen, device="cuda") * std).to(torch.bfloat16)
+
+    ones = torch.ones(d, dtype=torch.bfloat16, device="cuda")
+    blocks = [{"w_in": rnd((3 * D + 2 * F, D), D ** -0.5), "w_out": rnd((D, D + F), (D + F) ** -0.5),
+               "q_scale": ones, "k_scale": ones} for _ in range(2 * sc.n_stage1 + sc.n_joint)]
+    t = {"img_in_w": rnd((D, C), C ** -0.5), "img_in_b": rnd((D,), 0.1), "ref_in_w": None,
+         "ref_in_b": None, "txt_in_w": rnd((D, T), T ** -0.5), "txt_in_b": rnd((D,), 0.1),
+         "t_w1": rnd((D, 256), 1 / 16), "t_b1": rnd((D,), 0.1), "t_w2": rnd((D, D), D ** -0.5),
+         "t_b2": rnd((D,), 0.1),
+         "mod_w": [rnd((3 * D, D), (0.1 / D) ** 0.5) for _ in range(4)],
+         "mod_b": [rnd((3 * D,), 0.1) for _ in range(4)],
+         "out_mod_w": rnd((2 * D, D), (0.1 / D) ** 0.5), "out_mod_b": rnd((2 * D,), 0.1),
+         "out_w": rnd((C, D), D ** -0.5), "out_b": rnd((C,), 0.1)}
+    from flow_matching_diffusion_adaln_amd import inputs
+    cfg_joint = configs.BlockConfig("joint", 0, (configs.Stream("image", n_img, (sc.image_side,) * 2, sc.t),
+                                                 configs.Stream("text", n_txt)))
+    pos = torch.from_numpy(inputs.positions(cfg_joint)).cuda()
+    tc, tn = rnd((n_txt, T), 1.0), rnd((n_txt, T), 1.0)
+    z0 = rnd((n_img, C), 1.0)
+
+    def model_for(scale):
+        st = ops.make_stack_desc(n_img, n_txt, sc.n_stage1, sc.n_stage1, sc.n_joint, scale)
+        return ops.Model(ops.make_model_desc(st, C, T), t, blocks)
+
+    guided = model_for(sc.cfg_scale)
+    ws = ops.alloc_sampler_workspace(guided.desc)
+    sig = ops.flow_sigmas(50, 6.93)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ops.sampler_prepare(guided, tc, tn, None, pos, ws)
+    torch.cuda.synchronize()
+    prep_ms = (time.perf_counter() - t0) * 1e3
+    z = z0.clone()
+    for i in range(warmup):
+        ops.sampler_step(guided, z, sig[i], sig[i + 1], pos, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ops.sampler_step(guided, z, sig[warmup + i], sig[warmup + i + 1], pos, ws)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / steps
+    assert bool(torch.isfinite(z.float()).all())
+
+    plain = model_for(1.0)
+    sig16 = ops.flow_sigmas(16, 6.93)
+    z = z0.clone()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ops.sampler_prepare(plain, tc, None, None, pos, ws)
+    for i in range(16):
+        ops.sampler_step(plain, z, sig16[i], sig16[i + 1], pos, ws)
+    torch.cuda.synchronize()
+    gen16_s = time.perf_counter() - t0
+    assert bool(torch.isfinite(z.float()).all())
+    return {
+        "workload": f"c5 sampler: 1024^2 latent ({n_img} tokens x {C} ch), {n_txt} text tokens "
+                    f"({T}-wide features), {sc.n_stage1}+{sc.n_stage1}+{sc.n_joint} blocks, "
+                    f"shift 6.93",
+        "prepare_ms_guided": round(prep_ms, 2),
+        "ms_per_guided_step": round(step_ms, 3),
+        "guided_50_step_transformer_s": round((prep_ms + 50 * step_ms) / 1e3, 3),
+        "unguided_16_step_generation_s": round(gen16_s, 3),
         "steps": steps, "warmup": warmup,
     }
 
@@ -352,6 +432,8 @@ def main():
 
     if not args.no_stack:
         result["stack_c5"] = stack_c5(torch, configs, ops, steps=3, warmup=1)
+    if not args.no_stack:
+        result["sampler_c5"] = sampler_c5(torch, configs, ops, steps=3, warmup=1)
     if not args.no_long:
         result["block_edit2048"] = block_long(torch, configs, ops, timing, steps=5, warmup=1)
 

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdit.so")
-SOURCES = ["abi.cpp", "adaln.hip", "rope.hip", "attn.hip", "gemm.hip", "cfg.hip"]
+SOURCES = ["abi.cpp", "adaln.hip", "rope.hip", "attn.hip", "gemm.hip", "cfg.hip", "sampler.hip"]
 ARCH = "gfx950"
 
 

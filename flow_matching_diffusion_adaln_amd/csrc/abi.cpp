@@ -203,6 +203,144 @@ int check_params(const dit_block_params& p) {
   return DIT_OK;
 }
 
+
+// ---- sampler ---------------------------------------------------------------
+
+constexpr int kMaxSteps = 100000;
+constexpr int kGroupImg = 0, kGroupRef = 1, kGroupTxt = 2, kGroupJoint = 3;
+
+// Workspace of the sampler: the stack's (block workspace + one activation
+// buffer per branch) first, then the rows prepared once per generation, the
+// timestep path and the two branches' velocities.
+struct SamplerWs {
+  char* stack;                 // block workspace, then xc, xn
+  size_t block_ws;             // bytes of the block workspace
+  char* xc;                    // [N, D] prompt branch
+  char* xn;                    // [N, D] negative branch
+  uint16_t *txt_c, *txt_n;     // [n_txt, D] prepared text rows
+  uint16_t* ref;               // [n_ref, D] prepared reference rows
+  uint16_t* phi;               // [4, 256] timestep sinusoids
+  uint16_t *th, *te;           // [2, D] timestep MLP hidden and output (rows: t, 0)
+  uint16_t *mod_img, *mod_ref, *mod_txt;  // [3, D]
+  uint16_t* mod_joint;         // [3, 3, D]
+  uint16_t* out_mod;           // [2, D]
+  uint16_t* u;                 // [n_img, D] normalized image rows
+  uint16_t *v_c, *v_n;         // [n_img, C]
+  size_t bytes;
+};
+
+SamplerWs sampler_layout(const dit_model_desc* d, const Shape& js, void* base) {
+  const dit_stack_desc& st = d->stack;
+  const size_t D = js.D, row = D * 2, C = d->latent_ch;
+  char* p = static_cast<char*>(base);
+  SamplerWs w;
+  size_t off = 0;
+  auto take = [&](size_t n) -> char* {
+    char* q = p + off;
+    off += round_up(n);
+    return q;
+  };
+  w.block_ws = layout(js, nullptr).bytes;
+  w.stack = take(w.block_ws);
+  w.xc = take((size_t)js.N * row);
+  w.xn = take((size_t)js.N * row);
+  w.txt_c = reinterpret_cast<uint16_t*>(take((size_t)st.n_txt * row));
+  w.txt_n = reinterpret_cast<uint16_t*>(take((size_t)st.n_txt * row));
+  w.ref = reinterpret_cast<uint16_t*>(take((size_t)st.n_ref * row));
+  w.phi = reinterpret_cast<uint16_t*>(take(4 * DIT_TIME_DIM * 2));
+  w.th = reinterpret_cast<uint16_t*>(take(2 * row));
+  w.te = reinterpret_cast<uint16_t*>(take(2 * row));
+  w.mod_img = reinterpret_cast<uint16_t*>(take(3 * row));
+  w.mod_ref = reinterpret_cast<uint16_t*>(take(3 * row));
+  w.mod_txt = reinterpret_cast<uint16_t*>(take(3 * row));
+  w.mod_joint = reinterpret_cast<uint16_t*>(take(9 * row));
+  w.out_mod = reinterpret_cast<uint16_t*>(take(2 * row));
+  w.u = reinterpret_cast<uint16_t*>(take((size_t)st.n_img * row));
+  w.v_c = reinterpret_cast<uint16_t*>(take((size_t)st.n_img * C * 2));
+  w.v_n = reinterpret_cast<uint16_t*>(take((size_t)st.n_img * C * 2));
+  w.bytes = off;
+  return w;
+}
+
+int check_model(const dit_model_desc* d, Shape* js, size_t* bytes) {
+  if (!d) return DIT_ERR_NULL;
+  size_t stack_bytes = 0;
+  int rc = check_stack(&d->stack, js, &stack_bytes);
+  if (rc != DIT_OK) return rc;
+  if (d->latent_ch <= 0 || d->text_dim <= 0) return DIT_ERR_SHAPE;
+  if (d->latent_ch % 32 != 0 || d->latent_ch > 8192 || d->text_dim % 16 != 0 ||
+      d->text_dim > (1 << 20))
+    return DIT_ERR_UNSUPPORTED;
+  *bytes = sampler_layout(d, *js, nullptr).bytes;
+  return DIT_OK;
+}
+
+bool bad_ptr(const void* p) { return p == nullptr; }
+
+int check_weights(const dit_model_desc* d, const dit_model_weights* w) {
+  if (!w) return DIT_ERR_NULL;
+  const bool refs = d->stack.n_ref > 0;
+  const void* need[] = {w->img_in_w, w->img_in_b, w->txt_in_w,  w->txt_in_b,  w->t_w1,
+                        w->t_b1,     w->t_w2,     w->t_b2,      w->out_mod_w, w->out_mod_b,
+                        w->out_w,    w->out_b};
+  for (const void* p : need)
+    if (bad_ptr(p)) return DIT_ERR_NULL;
+  for (int g = 0; g < DIT_N_GROUPS; ++g) {
+    if (g == kGroupRef && !refs) continue;
+    if (bad_ptr(w->mod_w[g]) || bad_ptr(w->mod_b[g])) return DIT_ERR_NULL;
+    if (misaligned(w->mod_w[g]) || misaligned(w->mod_b[g])) return DIT_ERR_ALIGN;
+  }
+  if (refs && (bad_ptr(w->ref_in_w) || bad_ptr(w->ref_in_b))) return DIT_ERR_NULL;
+  for (const void* p : need)
+    if (misaligned(p)) return DIT_ERR_ALIGN;
+  if (refs && (misaligned(w->ref_in_w) || misaligned(w->ref_in_b))) return DIT_ERR_ALIGN;
+  const dit_stack_desc& st = d->stack;
+  const int n_blocks = st.n_img_blocks + st.n_ref_blocks + st.n_txt_blocks + st.n_joint_blocks;
+  if (n_blocks > 0 && !w->blocks) return DIT_ERR_NULL;
+  for (int i = 0; i < n_blocks; ++i) {
+    const dit_block_weights& b = w->blocks[i];
+    if (!b.w_in || !b.w_out || !b.q_scale || !b.k_scale) return DIT_ERR_NULL;
+    if (misaligned(b.w_in) || misaligned(b.w_out) || misaligned(b.q_scale) ||
+        misaligned(b.k_scale))
+      return DIT_ERR_ALIGN;
+  }
+  return DIT_OK;
+}
+
+int lin(const void* x, const void* w, const void* b, void* y, int M, int N, int K, int ldy,
+        int act, hipStream_t stream) {
+  return hip_status(dit::launch_linear(static_cast<const uint16_t*>(x),
+                                       static_cast<const uint16_t*>(w),
+                                       static_cast<const uint16_t*>(b), static_cast<uint16_t*>(y),
+                                       M, N, K, K, ldy, act, stream));
+}
+
+// e (rows: the given timesteps) = SiLU(W2 SiLU(W1 phi(t) + b1) + b2) into ws.te
+int time_embedding(const dit_model_weights* w, const SamplerWs& ws, const double* t, int n_t,
+                   int D, hipStream_t stream) {
+  int rc = hip_status(dit::launch_sinusoid(t, n_t, DIT_TIME_DIM, 1000.0, 10000.0, ws.phi, stream));
+  if (rc == DIT_OK) rc = lin(ws.phi, w->t_w1, w->t_b1, ws.th, n_t, D, DIT_TIME_DIM, D, 1, stream);
+  if (rc == DIT_OK) rc = lin(ws.th, w->t_w2, w->t_b2, ws.te, n_t, D, D, D, 1, stream);
+  return rc;
+}
+
+// Runs blocks [first, first + n) of the model on rows h with one modulation.
+int run_blocks(const dit_model_weights* w, const SamplerWs& ws, const dit_block_desc& d,
+               int first, int n, const uint16_t* mod, char* h, const int32_t* pos,
+               hipStream_t stream) {
+  for (int i = 0; i < n; ++i) {
+    const dit_block_weights& b = w->blocks[first + i];
+    const int rc = block_fwd(&d, h, mod, pos, b.w_in, b.w_out, b.q_scale, b.k_scale, h, ws.stack,
+                             ws.block_ws, stream, nullptr);
+    if (rc != DIT_OK) return rc;
+  }
+  return DIT_OK;
+}
+
+int dcopy(void* dst, const void* src, size_t n, hipStream_t stream) {
+  return hip_status(hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -390,6 +528,183 @@ int dit_stack_fwd(const dit_stack_desc* desc, const void* x_img, const void* x_r
                                             static_cast<uint16_t*>(v_img),
                                             (long long)desc->n_img * js.D, desc->cfg_scale,
                                             stream));
+}
+
+int dit_flow_sigmas(int32_t n_steps, double alpha, double* sigmas) {
+  if (n_steps < 1 || n_steps > kMaxSteps) return DIT_ERR_SHAPE;
+  if (!isfinite(alpha) || alpha <= 0.0) return DIT_ERR_ARG;
+  if (!sigmas) return DIT_ERR_NULL;
+  for (int i = 0; i <= n_steps; ++i) {
+    const double u = 1.0 - (double)i / n_steps;
+    sigmas[i] = alpha * u / (1.0 + (alpha - 1.0) * u);
+  }
+  return DIT_OK;
+}
+
+int dit_sampler_workspace_bytes(const dit_model_desc* desc, size_t* bytes) {
+  Shape js;
+  size_t need = 0;
+  const int rc = check_model(desc, &js, &need);
+  if (rc != DIT_OK) return rc;
+  if (!bytes) return DIT_ERR_NULL;
+  *bytes = need;
+  return DIT_OK;
+}
+
+int dit_sampler_prepare(const dit_model_desc* desc, const dit_model_weights* weights,
+                        const void* txt_cond, const void* txt_neg, const void* ref_latent,
+                        const int32_t* pos, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  Shape js;
+  size_t need = 0;
+  int rc = check_model(desc, &js, &need);
+  if (rc != DIT_OK) return rc;
+  if ((rc = check_weights(desc, weights)) != DIT_OK) return rc;
+  const dit_stack_desc& st = desc->stack;
+  const bool guided = st.cfg_scale != 1.0f, refs = st.n_ref > 0;
+  if (!txt_cond || (guided && !txt_neg) || (refs && !ref_latent) || !pos || !workspace)
+    return DIT_ERR_NULL;
+  if (misaligned(txt_cond) || (guided && misaligned(txt_neg)) ||
+      (refs && misaligned(ref_latent)) || misaligned(pos) || misaligned(workspace))
+    return DIT_ERR_ALIGN;
+  if (workspace_bytes < need) return DIT_ERR_WORKSPACE;
+  const SamplerWs ws = sampler_layout(desc, js, workspace);
+  const int D = js.D;
+  const double t0 = 0.0;
+  if ((rc = time_embedding(weights, ws, &t0, 1, D, stream)) != DIT_OK) return rc;
+  // references: embedded and run through their blocks at t = 0
+  const int32_t* pos_ref = pos + (size_t)st.n_img * 4;
+  const int32_t* pos_txt = pos_ref + (size_t)st.n_ref * 4;
+  if (refs) {
+    const dit_block_desc dr = stack_block_desc(&st, 1, st.n_ref);
+    if ((rc = lin(ws.te, weights->mod_w[kGroupRef], weights->mod_b[kGroupRef], ws.mod_ref, 1,
+                  3 * D, D, 3 * D, 0, stream)) != DIT_OK ||
+        (rc = lin(ref_latent, weights->ref_in_w, weights->ref_in_b, ws.ref, st.n_ref, D,
+                  desc->latent_ch, D, 0, stream)) != DIT_OK ||
+        (rc = run_blocks(weights, ws, dr, st.n_img_blocks, st.n_ref_blocks, ws.mod_ref,
+                         reinterpret_cast<char*>(ws.ref), pos_ref, stream)) != DIT_OK)
+      return rc;
+  }
+  // text of each prompt: embedded and run through the text blocks at t = 0
+  const dit_block_desc dt = stack_block_desc(&st, 1, st.n_txt);
+  if ((rc = lin(ws.te, weights->mod_w[kGroupTxt], weights->mod_b[kGroupTxt], ws.mod_txt, 1,
+                3 * D, D, 3 * D, 0, stream)) != DIT_OK)
+    return rc;
+  const int first_txt = st.n_img_blocks + st.n_ref_blocks;
+  const void* feats[2] = {txt_cond, txt_neg};
+  uint16_t* rows[2] = {ws.txt_c, ws.txt_n};
+  for (int b = 0; b < (guided ? 2 : 1); ++b) {
+    if ((rc = lin(feats[b], weights->txt_in_w, weights->txt_in_b, rows[b], st.n_txt, D,
+                  desc->text_dim, D, 0, stream)) != DIT_OK ||
+        (rc = run_blocks(weights, ws, dt, first_txt, st.n_txt_blocks, ws.mod_txt,
+                         reinterpret_cast<char*>(rows[b]), pos_txt, stream)) != DIT_OK)
+      return rc;
+  }
+  return DIT_OK;
+}
+
+int dit_sampler_step(const dit_model_desc* desc, const dit_model_weights* weights, void* z,
+                     double sigma, double sigma_next, const int32_t* pos, void* v_out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Shape js;
+  size_t need = 0;
+  int rc = check_model(desc, &js, &need);
+  if (rc != DIT_OK) return rc;
+  if ((rc = check_weights(desc, weights)) != DIT_OK) return rc;
+  if (!isfinite(sigma) || !isfinite(sigma_next)) return DIT_ERR_ARG;
+  if (!z || !pos || !workspace) return DIT_ERR_NULL;
+  if (misaligned(z) || misaligned(pos) || misaligned(workspace) || (v_out && misaligned(v_out)))
+    return DIT_ERR_ALIGN;
+  if (workspace_bytes < need) return DIT_ERR_WORKSPACE;
+  const dit_stack_desc& st = desc->stack;
+  const bool guided = st.cfg_scale != 1.0f, refs = st.n_ref > 0;
+  const int D = js.D, C = desc->latent_ch;
+  const size_t zb = (size_t)st.n_img * C * 2;
+  if (overlaps(z, zb, workspace, need) || (v_out && overlaps(v_out, zb, workspace, need)) ||
+      (v_out && overlaps(v_out, zb, z, zb)))
+    return DIT_ERR_ARG;
+  const SamplerWs ws = sampler_layout(desc, js, workspace);
+  const size_t row = (size_t)D * 2;
+  const size_t img_bytes = (size_t)st.n_img * row, pre_bytes = img_bytes + (size_t)st.n_ref * row;
+  const size_t txt_bytes = (size_t)st.n_txt * row;
+
+  // timestep path: row 0 at sigma (image tokens), row 1 at t = 0 (the others)
+  const double ts[2] = {sigma, 0.0};
+  if ((rc = time_embedding(weights, ws, ts, 2, D, stream)) != DIT_OK) return rc;
+  if ((rc = lin(ws.te, weights->mod_w[kGroupImg], weights->mod_b[kGroupImg], ws.mod_img, 1,
+                3 * D, D, 3 * D, 0, stream)) != DIT_OK ||
+      (rc = lin(ws.te, weights->mod_w[kGroupJoint], weights->mod_b[kGroupJoint], ws.mod_joint, 2,
+                3 * D, D, 3 * D, 0, stream)) != DIT_OK ||
+      (rc = lin(ws.te, weights->out_mod_w, weights->out_mod_b, ws.out_mod, 1, 2 * D, D, 2 * D, 0,
+                stream)) != DIT_OK)
+    return rc;
+  // joint modulation per stream: image at sigma, reference and text at 0
+  if (refs && (rc = dcopy(ws.mod_joint + 6 * (size_t)D, ws.mod_joint + 3 * (size_t)D, 3 * row,
+                          stream)) != DIT_OK)
+    return rc;
+
+  // image tokens: embedded, then the stage-1 image blocks (shared by both branches)
+  const dit_block_desc di = stack_block_desc(&st, 1, st.n_img);
+  if ((rc = lin(z, weights->img_in_w, weights->img_in_b, ws.xc, st.n_img, D, C, D, 0,
+                stream)) != DIT_OK ||
+      (rc = run_blocks(weights, ws, di, 0, st.n_img_blocks, ws.mod_img, ws.xc, pos, stream)) !=
+          DIT_OK)
+    return rc;
+  if (refs && (rc = dcopy(ws.xc + img_bytes, ws.ref, pre_bytes - img_bytes, stream)) != DIT_OK)
+    return rc;
+  if ((rc = dcopy(ws.xc + pre_bytes, ws.txt_c, txt_bytes, stream)) != DIT_OK) return rc;
+  if (guided && ((rc = dcopy(ws.xn, ws.xc, pre_bytes, stream)) != DIT_OK ||
+                 (rc = dcopy(ws.xn + pre_bytes, ws.txt_n, txt_bytes, stream)) != DIT_OK))
+    return rc;
+
+  // joint blocks and output layers per branch
+  const dit_block_desc dj = joint_desc(&st);
+  const int first_joint = st.n_img_blocks + st.n_ref_blocks + st.n_txt_blocks;
+  char* hs[2] = {ws.xc, ws.xn};
+  uint16_t* vs[2] = {ws.v_c, ws.v_n};
+  for (int b = 0; b < (guided ? 2 : 1); ++b) {
+    if ((rc = run_blocks(weights, ws, dj, first_joint, st.n_joint_blocks, ws.mod_joint, hs[b],
+                         pos, stream)) != DIT_OK ||
+        (rc = hip_status(dit::launch_adaln(reinterpret_cast<const uint16_t*>(hs[b]), ws.out_mod,
+                                           ws.u, st.n_img, D, st.n_img, st.n_img, st.ln_eps,
+                                           stream))) != DIT_OK ||
+        (rc = lin(ws.u, weights->out_w, weights->out_b, vs[b], st.n_img, C, D, C, 0, stream)) !=
+            DIT_OK)
+      return rc;
+  }
+  // guided velocity and the Euler update of the latent
+  return hip_status(dit::launch_euler_cfg(static_cast<uint16_t*>(z), ws.v_c,
+                                          guided ? ws.v_n : nullptr,
+                                          static_cast<uint16_t*>(v_out), (long long)st.n_img * C,
+                                          st.cfg_scale, (float)(sigma_next - sigma), stream));
+}
+
+int dit_linear(int32_t M, int32_t N, int32_t K, const void* x, const void* w, const void* b,
+               int32_t act, void* y, hipStream_t stream) {
+  if (M < 0 || N <= 0 || K <= 0) return DIT_ERR_SHAPE;
+  if (N % 32 != 0 || K % 16 != 0) return DIT_ERR_UNSUPPORTED;
+  if ((long long)M * K * 2 >= kMaxBytes * 4 || (long long)N * K * 2 >= kMaxBytes)
+    return DIT_ERR_UNSUPPORTED;
+  if (act != 0 && act != 1) return DIT_ERR_ARG;
+  if (M == 0) return DIT_OK;
+  if (!x || !w || !y) return DIT_ERR_NULL;
+  if (misaligned(x) || misaligned(w) || (b && misaligned(b)) || misaligned(y))
+    return DIT_ERR_ALIGN;
+  const size_t yb = (size_t)M * N * 2;
+  if (overlaps(y, yb, x, (size_t)M * K * 2) || overlaps(y, yb, w, (size_t)N * K * 2) ||
+      (b && overlaps(y, yb, b, (size_t)N * 2)))
+    return DIT_ERR_ARG;
+  return lin(x, w, b, y, M, N, K, N, act, stream);
+}
+
+int dit_time_sinusoid(int32_t n_t, const double* t, void* out, hipStream_t stream) {
+  if (n_t < 1 || n_t > 4) return DIT_ERR_SHAPE;
+  if (!t || !out) return DIT_ERR_NULL;
+  if (misaligned(out)) return DIT_ERR_ALIGN;
+  for (int i = 0; i < n_t; ++i)
+    if (!isfinite(t[i])) return DIT_ERR_ARG;
+  return hip_status(dit::launch_sinusoid(t, n_t, DIT_TIME_DIM, 1000.0, 10000.0,
+                                         static_cast<uint16_t*>(out), stream));
 }
 
 const char* dit_status_str(int status) {

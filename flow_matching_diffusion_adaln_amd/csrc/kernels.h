@@ -37,4 +37,21 @@ hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, in
 hipError_t launch_cfg_combine(const uint16_t* cond, const uint16_t* neg, uint16_t* out,
                               long long n, float scale, hipStream_t stream);
 
+// y[m, n] = act(x[m, :] . w[n, :] + b[n]) (act 0: none, 1: SiLU), bf16 in and
+// out, fp32 accumulation.  w is [N, K] row-major; b may be null.  K must be
+// a multiple of 16, N of 32; row strides ldx, ldy in elements.
+hipError_t launch_linear(const uint16_t* x, const uint16_t* w, const uint16_t* b, uint16_t* y,
+                         int M, int N, int K, int ldx, int ldy, int act, hipStream_t stream);
+
+// out [n_t, dim] bf16: [cos | sin] of scale * t_r * max_period^(-i / (dim / 2)),
+// n_t <= 4, dim even.
+hipError_t launch_sinusoid(const double* t, int n_t, int dim, double scale, double max_period,
+                           uint16_t* out, hipStream_t stream);
+
+// z += dsigma * (neg + scale * (cond - neg)) over n bf16 values (n a multiple
+// of 8; neg null: dsigma * cond); v_out (optional) gets the guided velocity.
+hipError_t launch_euler_cfg(uint16_t* z, const uint16_t* cond, const uint16_t* neg,
+                            uint16_t* v_out, long long n, float scale, float dsigma,
+                            hipStream_t stream);
+
 }  // namespace dit

@@ -16,7 +16,11 @@ the pages' shapes stand in for them):
     (0, i // cols, i % cols, 0); a reference uses the same grid with l = 1;
     text token k is (k, 0, 0, 0), padding included.  This follows the 4-axis
     RoPE description in "Welcome FLUX.3 Image Klein in Diffusers", section
-    "How it works" (references share (h, w) with the output).
+    "How it works" (references share (h, w) with the output);
+  * the sampler's layers around the blocks (make_sampler_inputs): every
+    weight ~ N(0, 1/fan_in) except the modulation linears, N(0, 0.1/fan_in),
+    so shift / scale / gate come out at about the size above; biases
+    ~ N(0, 0.01); the latent, reference latents and text features ~ N(0, 1).
 """
 from __future__ import annotations
 
@@ -24,13 +28,14 @@ from typing import Dict
 
 import numpy as np
 
-from .configs import BlockConfig, STREAM_IMAGE, STREAM_REF, STREAM_TEXT
+from .configs import BlockConfig, STREAM_IMAGE, STREAM_REF, STREAM_TEXT, Stream
 
 TENSOR_X = 1
 TENSOR_MOD = 2
 TENSOR_W_IN = 3
 TENSOR_W_OUT = 4
 TENSOR_QKV = 5  # standalone attention inputs
+TENSOR_SAMPLER = 6
 
 _CHUNK = 1 << 22
 
@@ -141,3 +146,44 @@ def make_attn_inputs(n_tokens: int, n_heads: int, head_dim: int, seed: int = 0,
         "k": normal_bf16(shape, qk_std, seed, 100 + case, n_tokens, TENSOR_QKV, 1),
         "v": normal_bf16(shape, 1.0, seed, 100 + case, n_tokens, TENSOR_QKV, 2),
     }
+
+
+def make_sampler_inputs(n_img_side: int, n_ref_side: int, n_txt: int, blocks, seed: int = 0,
+                        width: int = 3072, n_heads: int = 24, head_dim: int = 128,
+                        mlp_hidden: int = 9216, latent_ch: int = 128, text_dim: int = 20480,
+                        time_dim: int = 256) -> Dict:
+    """Host inputs of the sampler as bf16 bits: the model's layers around the
+    blocks, the blocks' weights (blocks = (n_img, n_ref, n_txt, n_joint)
+    counts), the latent z, text features of both prompts, one reference of
+    n_ref_side^2 tokens (none when 0) and the joint positions."""
+    D, F, C, T = width, mlp_hidden, latent_ch, text_dim
+    key = (seed, TENSOR_SAMPLER)
+    k = [0]
+
+    def draw(shape, std):
+        k[0] += 1
+        return normal_bf16(shape, std, *key, k[0])
+
+    m = {"img_in_w": draw((D, C), C ** -0.5), "img_in_b": draw((D,), 0.1),
+         "ref_in_w": draw((D, C), C ** -0.5), "ref_in_b": draw((D,), 0.1),
+         "txt_in_w": draw((D, T), T ** -0.5), "txt_in_b": draw((D,), 0.1),
+         "t_w1": draw((D, time_dim), time_dim ** -0.5), "t_b1": draw((D,), 0.1),
+         "t_w2": draw((D, D), D ** -0.5), "t_b2": draw((D,), 0.1),
+         "mod_w": [draw((3 * D, D), (0.1 / D) ** 0.5) for _ in range(4)],
+         "mod_b": [draw((3 * D,), 0.1) for _ in range(4)],
+         "out_mod_w": draw((2 * D, D), (0.1 / D) ** 0.5), "out_mod_b": draw((2 * D,), 0.1),
+         "out_w": draw((C, D), D ** -0.5), "out_b": draw((C,), 0.1)}
+    one = f64_to_bf16_bits(np.ones(head_dim))
+    m["blocks"] = [{"w_in": draw((3 * D + 2 * F, D), D ** -0.5),
+                    "w_out": draw((D, D + F), (D + F) ** -0.5),
+                    "q_scale": one.copy(), "k_scale": one.copy()} for _ in range(sum(blocks))]
+    n_img, n_ref = n_img_side ** 2, n_ref_side ** 2
+    streams = [Stream(STREAM_IMAGE, n_img, (n_img_side, n_img_side), 0.0)]
+    if n_ref:
+        streams.append(Stream(STREAM_REF, n_ref, (n_ref_side, n_ref_side), 0.0))
+    streams.append(Stream(STREAM_TEXT, n_txt))
+    return {"model": m, "z": draw((n_img, C), 1.0), "txt_cond": draw((n_txt, T), 1.0),
+            "txt_neg": draw((n_txt, T), 1.0),
+            "ref_latent": draw((n_ref, C), 1.0) if n_ref else None,
+            "pos": positions(BlockConfig("sampler", 0, tuple(streams), width, n_heads, head_dim,
+                                         mlp_hidden))}

@@ -24,7 +24,10 @@ N_STAGES = 5
 STAGES = ("adaln", "gemm_in", "rope", "attn", "gemm_out")
 EXPORTS = ("dit_block_workspace_bytes", "dit_block_fwd", "dit_block_fwd_events", "dit_attn_fwd",
            "rope4_apply", "adaln_mod", "dit_stack_workspace_bytes", "dit_stack_fwd",
-           "dit_status_str")
+           "dit_flow_sigmas", "dit_sampler_workspace_bytes", "dit_sampler_prepare",
+           "dit_sampler_step", "dit_linear", "dit_time_sinusoid", "dit_status_str")
+N_GROUPS = 4        # block groups with their own modulation: stage-1 image, reference, text; joint
+TIME_DIM = 256
 
 
 class BlockDesc(ctypes.Structure):
@@ -66,6 +69,28 @@ class BlockParams(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in ("mod", "w_in", "w_out", "q_scale", "k_scale")]
 
 
+class ModelDesc(ctypes.Structure):
+    _fields_ = [("stack", StackDesc), ("latent_ch", ctypes.c_int32), ("text_dim", ctypes.c_int32)]
+
+
+BLOCK_WEIGHTS = ("w_in", "w_out", "q_scale", "k_scale")
+
+
+class BlockWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in BLOCK_WEIGHTS]
+
+
+MODEL_TENSORS = ("img_in_w", "img_in_b", "ref_in_w", "ref_in_b", "txt_in_w", "txt_in_b",
+                 "t_w1", "t_b1", "t_w2", "t_b2")
+
+
+class ModelWeights(ctypes.Structure):
+    _fields_ = ([(name, ctypes.c_void_p) for name in MODEL_TENSORS]
+                + [("mod_w", ctypes.c_void_p * N_GROUPS), ("mod_b", ctypes.c_void_p * N_GROUPS)]
+                + [(name, ctypes.c_void_p) for name in ("out_mod_w", "out_mod_b", "out_w", "out_b")]
+                + [("blocks", ctypes.POINTER(BlockWeights))])
+
+
 _lib = None
 
 
@@ -89,6 +114,14 @@ def load_library() -> ctypes.CDLL:
     lib.dit_stack_workspace_bytes.argtypes = [stack_p, ctypes.POINTER(sz)]
     lib.dit_stack_fwd.argtypes = [stack_p, vp, vp, vp, vp, vp, ctypes.POINTER(BlockParams), vp, vp,
                                   sz, vp]
+    model_p, weights_p = ctypes.POINTER(ModelDesc), ctypes.POINTER(ModelWeights)
+    f64 = ctypes.c_double
+    lib.dit_flow_sigmas.argtypes = [i32, f64, ctypes.POINTER(f64)]
+    lib.dit_sampler_workspace_bytes.argtypes = [model_p, ctypes.POINTER(sz)]
+    lib.dit_sampler_prepare.argtypes = [model_p, weights_p, vp, vp, vp, vp, vp, sz, vp]
+    lib.dit_sampler_step.argtypes = [model_p, weights_p, vp, f64, f64, vp, vp, vp, sz, vp]
+    lib.dit_linear.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp]
+    lib.dit_time_sinusoid.argtypes = [i32, ctypes.POINTER(f64), vp, vp]
     lib.dit_status_str.argtypes = [ctypes.c_int]
     lib.dit_status_str.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -312,3 +345,137 @@ def stack_fwd(desc: StackDesc, x_img, x_txt_cond, x_txt_neg, pos, blocks, v_img=
         ctypes.c_void_p(pos.data_ptr()), arr, _ptr(v_img), _ptr(workspace),
         ctypes.c_size_t(workspace.numel()), _stream(stream)))
     return v_img
+
+
+# ---- flow-matching sampler ------------------------------------------------------
+
+def flow_sigmas(n_steps: int, alpha: float = 6.93):
+    """The n_steps + 1 sigmas of the shifted schedule (dit_flow_sigmas), as a list."""
+    out = (ctypes.c_double * (n_steps + 1))()
+    _check(load_library().dit_flow_sigmas(n_steps, ctypes.c_double(alpha), out))
+    return list(out)
+
+
+def make_model_desc(stack: StackDesc, latent_ch: int = 128, text_dim: int = 20480) -> ModelDesc:
+    d = ModelDesc()
+    d.stack = stack
+    d.latent_ch, d.text_dim = latent_ch, text_dim
+    return d
+
+
+def sampler_workspace_bytes(desc: ModelDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().dit_sampler_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+class Model:
+    """Device weights of the model around the blocks, marshalled once into the
+    C structs.  tensors: dict with the MODEL_TENSORS names plus out_mod_w,
+    out_mod_b, out_w, out_b and lists mod_w, mod_b (N_GROUPS each);
+    blocks: list of dicts with the BLOCK_WEIGHTS names (groups in order
+    image, reference, text, joint).  ref_in_* and the reference group's
+    modulation may be None without references."""
+
+    def __init__(self, desc: ModelDesc, tensors, blocks):
+        st = desc.stack
+        D, F, d, C, T = st.width, st.mlp_hidden, st.head_dim, desc.latent_ch, desc.text_dim
+        refs = st.n_ref > 0
+        shapes = {"img_in_w": (D, C), "img_in_b": (D,), "ref_in_w": (D, C), "ref_in_b": (D,),
+                  "txt_in_w": (D, T), "txt_in_b": (D,), "t_w1": (D, TIME_DIM), "t_b1": (D,),
+                  "t_w2": (D, D), "t_b2": (D,), "out_mod_w": (2 * D, D), "out_mod_b": (2 * D,),
+                  "out_w": (C, D), "out_b": (C,)}
+        w = ModelWeights()
+        for name, shape in shapes.items():
+            t = tensors.get(name)
+            if t is None and name.startswith("ref_in") and not refs:
+                continue
+            _bf16(t, shape, name)
+            setattr(w, name, t.data_ptr())
+        for g in range(N_GROUPS):
+            if tensors["mod_w"][g] is None and g == 1 and not refs:
+                continue
+            _bf16(tensors["mod_w"][g], (3 * D, D), f"mod_w[{g}]")
+            _bf16(tensors["mod_b"][g], (3 * D,), f"mod_b[{g}]")
+            w.mod_w[g] = tensors["mod_w"][g].data_ptr()
+            w.mod_b[g] = tensors["mod_b"][g].data_ptr()
+        n_blocks = st.n_img_blocks + st.n_ref_blocks + st.n_txt_blocks + st.n_joint_blocks
+        if len(blocks) != n_blocks:
+            raise ValueError(f"expected {n_blocks} blocks, got {len(blocks)}")
+        self._blocks = (BlockWeights * max(n_blocks, 1))()
+        for i, b in enumerate(blocks):
+            _bf16(b["w_in"], (3 * D + 2 * F, D), f"blocks[{i}].w_in")
+            _bf16(b["w_out"], (D, D + F), f"blocks[{i}].w_out")
+            _bf16(b["q_scale"], (d,), f"blocks[{i}].q_scale")
+            _bf16(b["k_scale"], (d,), f"blocks[{i}].k_scale")
+            for name in BLOCK_WEIGHTS:
+                setattr(self._blocks[i], name, b[name].data_ptr())
+        w.blocks = self._blocks
+        self.weights = w
+        self.desc = desc
+        self._keep = (tensors, blocks)  # the device memory the pointers refer to
+
+
+def _pos_check(pos, n):
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (n, 4) or not pos.is_cuda \
+            or not pos.is_contiguous():
+        raise ValueError(f"pos must be a contiguous int32 [{n}, 4] GPU tensor")
+
+
+def alloc_sampler_workspace(desc: ModelDesc, device="cuda") -> torch.Tensor:
+    return torch.empty(sampler_workspace_bytes(desc), dtype=torch.uint8, device=device)
+
+
+def sampler_prepare(model: Model, txt_cond, txt_neg, ref_latent, pos, workspace, stream=None):
+    st, desc = model.desc.stack, model.desc
+    _bf16(txt_cond, (st.n_txt, desc.text_dim), "txt_cond")
+    if txt_neg is not None:
+        _bf16(txt_neg, (st.n_txt, desc.text_dim), "txt_neg")
+    if ref_latent is not None:
+        _bf16(ref_latent, (st.n_ref, desc.latent_ch), "ref_latent")
+    _pos_check(pos, st.n_img + st.n_ref + st.n_txt)
+    _check(load_library().dit_sampler_prepare(
+        ctypes.byref(desc), ctypes.byref(model.weights), _ptr(txt_cond), _ptr(txt_neg),
+        _ptr(ref_latent), ctypes.c_void_p(pos.data_ptr()), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel()), _stream(stream)))
+
+
+def sampler_step(model: Model, z, sigma: float, sigma_next: float, pos, workspace, v_out=None,
+                 stream=None):
+    """In place: z <- z + (sigma_next - sigma) * guided velocity (dit_sampler_step)."""
+    st, desc = model.desc.stack, model.desc
+    _bf16(z, (st.n_img, desc.latent_ch), "z")
+    if v_out is not None:
+        _bf16(v_out, (st.n_img, desc.latent_ch), "v_out")
+    _pos_check(pos, st.n_img + st.n_ref + st.n_txt)
+    _check(load_library().dit_sampler_step(
+        ctypes.byref(desc), ctypes.byref(model.weights), _ptr(z), ctypes.c_double(sigma),
+        ctypes.c_double(sigma_next), ctypes.c_void_p(pos.data_ptr()), _ptr(v_out),
+        _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return z
+
+
+def linear(x, w, b=None, act: int = 0, y=None, stream=None) -> torch.Tensor:
+    """y = act(x w^T + b) (dit_linear); x [M, K], w [N, K], b [N]."""
+    M, K = x.shape
+    N = w.shape[0]
+    _bf16(x, (M, K), "x")
+    _bf16(w, (N, K), "w")
+    if b is not None:
+        _bf16(b, (N,), "b")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _bf16(y, (M, N), "y")
+    _check(load_library().dit_linear(M, N, K, _ptr(x), _ptr(w), _ptr(b), act, _ptr(y),
+                                     _stream(stream)))
+    return y
+
+
+def time_sinusoid(ts, out=None, stream=None) -> torch.Tensor:
+    """out [len(ts), 256]: the timestep sinusoids (dit_time_sinusoid)."""
+    n = len(ts)
+    arr = (ctypes.c_double * max(n, 1))(*ts)
+    if out is None:
+        out = torch.empty((n, TIME_DIM), dtype=torch.bfloat16, device="cuda")
+    _check(load_library().dit_time_sinusoid(n, arr, _ptr(out), _stream(stream)))
+    return out

@@ -224,6 +224,114 @@ int dit_stack_fwd(const dit_stack_desc* desc, const void* x_img, const void* x_r
                   const dit_block_params* blocks, void* v_img, void* workspace,
                   size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Flow-matching sampler around the stack --------------------------------
+ * One Euler step of the latent from sigma to sigma_next, with the model's
+ * layers around the stack.  What the pages fix: the schedule's rational
+ * shift (alpha = 6.93: the DiffSynth-Studio FLUX.3 page, "Model Inference";
+ * 44 of 50 steps above sigma = 0.5: "Welcome FLUX.3 Image Klein in
+ * Diffusers", "How it works"), image tokens at the step's timestep and text
+ * and reference tokens at t = 0, image tokens alone reaching the output
+ * layers, 128-channel latent tokens and 20,480-wide text features (same
+ * section), the embedders and proj_out by name (same page, the LoRA target
+ * list) and neg + scale * (cond - neg) on the velocities (the miles page,
+ * section 3).  Read where the pages are silent: every embedder and proj_out
+ * is a linear layer with bias; the timestep t = sigma is embedded as 256
+ * sinusoids [cos | sin] of 1000 t 10000^(-i/128), then Linear(256, D) + SiLU,
+ * Linear(D, D) + SiLU = e; each block group (stage-1 image, reference, text;
+ * joint) has one Linear(D, 3D) of e giving (shift, scale, gate) to all its
+ * blocks, the joint group's applied per stream to that stream's e; the output
+ * layers are LayerNorm(no affine) * (1 + scale) + shift with (shift, scale) =
+ * Linear(D, 2D) of the image e, then proj_out; the velocity is dz / dsigma.
+ * Every tensor is bf16 (fp32 accumulation), the update z + dsigma v is taken
+ * in fp32 and rounded. */
+
+#define DIT_N_GROUPS 4 /* block groups: stage-1 image, reference, text; joint */
+#define DIT_TIME_DIM 256
+
+typedef struct dit_model_desc {
+  dit_stack_desc stack; /* tokens, block counts, widths, eps and cfg_scale          */
+  int32_t latent_ch;    /* C, channels of a latent token (128): a multiple of 32,   */
+                        /* at most 8192                                             */
+  int32_t text_dim;     /* width of a text feature (20480): a multiple of 16        */
+} dit_model_desc;
+
+/* Device pointers of one block's weights (its modulation comes from its group). */
+typedef struct dit_block_weights {
+  const void* w_in;    /* bf16 [3D + 2F, D] */
+  const void* w_out;   /* bf16 [D, D + F]   */
+  const void* q_scale; /* bf16 [d]          */
+  const void* k_scale; /* bf16 [d]          */
+} dit_block_weights;
+
+/* Device pointers of the layers around the blocks, all bf16, [out, in]. */
+typedef struct dit_model_weights {
+  const void* img_in_w;                /* [D, C]  x_embedders.image                       */
+  const void* img_in_b;                /* [D]                                             */
+  const void* ref_in_w;                /* [D, C]  x_embedders.image_cond (n_ref > 0 only) */
+  const void* ref_in_b;                /* [D]                                             */
+  const void* txt_in_w;                /* [D, text_dim]  context_embedder                 */
+  const void* txt_in_b;                /* [D]                                             */
+  const void* t_w1;                    /* [D, 256]  timestep MLP, first layer             */
+  const void* t_b1;                    /* [D]                                             */
+  const void* t_w2;                    /* [D, D]    second layer                          */
+  const void* t_b2;                    /* [D]                                             */
+  const void* mod_w[DIT_N_GROUPS];     /* [3D, D]  (shift | scale | gate) per group       */
+  const void* mod_b[DIT_N_GROUPS];     /* [3D]                                            */
+  const void* out_mod_w;               /* [2D, D]  (shift | scale) of the output norm     */
+  const void* out_mod_b;               /* [2D]                                            */
+  const void* out_w;                   /* [C, D]   proj_out                               */
+  const void* out_b;                   /* [C]                                             */
+  const dit_block_weights* blocks;     /* host array: n_img_blocks + n_ref_blocks +       */
+                                       /* n_txt_blocks + n_joint_blocks, in that order    */
+} dit_model_weights;
+
+/* The n_steps + 1 sigmas of the shifted schedule into host memory:
+ * sigma_i = alpha u / (1 + (alpha - 1) u), u = 1 - i / n_steps (1 down to 0).
+ * n_steps in [1, 100000], alpha finite and > 0. */
+int dit_flow_sigmas(int32_t n_steps, double alpha, double* sigmas);
+
+/* Bytes of device workspace the sampler needs: the stack's workspace plus the
+ * prepared text and reference rows, the timestep path and the velocities.
+ * The same workspace must be passed to dit_sampler_prepare and every
+ * following dit_sampler_step: it carries the prepared rows between calls. */
+int dit_sampler_workspace_bytes(const dit_model_desc* desc, size_t* bytes);
+
+/* The step-invariant part of sampling, once per generation: the text
+ * features of both prompts and the reference latents embedded and run
+ * through their stage-1 blocks at t = 0 (text and reference tokens always
+ * get t = 0, so these rows are the same at every step).
+ *   txt_cond    bf16 [n_txt, text_dim]  text features of the prompt
+ *   txt_neg     bf16 [n_txt, text_dim]  of the negative prompt (null when
+ *                                       cfg_scale == 1)
+ *   ref_latent  bf16 [n_ref, C]         reference latent tokens (null when
+ *                                       n_ref == 0)
+ *   pos         int32 [N, 4]            (t, h, w, l) in [image | reference | text]
+ * Writes only the workspace. */
+int dit_sampler_prepare(const dit_model_desc* desc, const dit_model_weights* weights,
+                        const void* txt_cond, const void* txt_neg, const void* ref_latent,
+                        const int32_t* pos, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* One guided Euler step, in place on the latent:
+ *   z      bf16 [n_img, C]  in: the latent at sigma; out: at sigma_next
+ *   v_out  bf16 [n_img, C]  optional: the guided velocity
+ * sigma and sigma_next finite (the sampler passes consecutive entries of
+ * dit_flow_sigmas).  Needs a workspace prepared by dit_sampler_prepare with
+ * the same desc, weights and pos. */
+int dit_sampler_step(const dit_model_desc* desc, const dit_model_weights* weights, void* z,
+                     double sigma, double sigma_next, const int32_t* pos, void* v_out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* y = act(x w^T + b), a linear layer as the sampler runs it (bf16, fp32
+ * accumulation): x [M, K], w [N, K], b [N] or null, y [M, N], act 0 (none) or
+ * 1 (SiLU after the bias).  K a multiple of 16, N of 32; y must not overlap x,
+ * w or b. */
+int dit_linear(int32_t M, int32_t N, int32_t K, const void* x, const void* w, const void* b,
+               int32_t act, void* y, hipStream_t stream);
+
+/* out bf16 [n_t, 256]: the timestep sinusoids of n_t (1..4) host values t. */
+int dit_time_sinusoid(int32_t n_t, const double* t, void* out, hipStream_t stream);
+
 /* Static name of a status code ("DIT_OK", "DIT_ERR_SHAPE: ...", ...). */
 const char* dit_status_str(int status);
 

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from flow_matching_diffusion_adaln_amd import ops
@@ -258,3 +259,154 @@ def test_stack_fwd_host_errors(lib):
     assert stack_call(lib, r, x_ref=0) == NULL
     assert stack_call(lib, r, x_ref=BAD) == ALIGN
     assert stack_call(lib, r, blocks="bad_null") == NULL
+
+
+# ---- sampler ---------------------------------------------------------------------
+
+def test_sampler_struct_layout():
+    assert ctypes.sizeof(ops.ModelDesc) == 68
+    assert ctypes.sizeof(ops.BlockWeights) == 32
+    assert ctypes.sizeof(ops.ModelWeights) == 23 * 8
+
+
+def test_flow_sigmas_match_the_oracle_and_the_pages_count(lib):
+    import oracle
+    for n, a in ((50, 6.93), (16, 6.93), (10, 3.0), (1, 6.93), (7, 1.0)):
+        got = np.array(ops.flow_sigmas(n, a))
+        want = oracle.flow_sigmas(n, a)
+        assert got[0] == 1.0 and got[-1] == 0.0
+        assert np.allclose(got, want, rtol=1e-15, atol=0)
+    assert int((np.array(ops.flow_sigmas(50, 6.93))[:50] > 0.5).sum()) == 44
+    out = (ctypes.c_double * 4)()
+    assert lib.dit_flow_sigmas(0, 6.93, out) == SHAPE
+    assert lib.dit_flow_sigmas(3, float("nan"), out) == ARG
+    assert lib.dit_flow_sigmas(3, -1.0, out) == ARG
+    assert lib.dit_flow_sigmas(3, 6.93, None) == NULL
+
+
+def model_desc(n_img=256, n_ref=0, n_txt=80, blocks=(1, 0, 1, 2), scale=4.0, **kw):
+    st = ops.make_stack_desc(n_img, n_txt, blocks[0], blocks[2], blocks[3], scale, n_ref=n_ref,
+                             n_ref_blocks=blocks[1])
+    return ops.make_model_desc(st, **kw)
+
+
+def sampler_ws(lib, d):
+    n = ctypes.c_size_t(0)
+    rc = lib.dit_sampler_workspace_bytes(ctypes.byref(d), ctypes.byref(n))
+    return rc, n.value
+
+
+def test_sampler_workspace_bytes(lib):
+    d = model_desc(4096, 0, 160)
+    rc, n = sampler_ws(lib, d)
+    assert rc == OK
+    _, ns = stack_ws(lib, d.stack)
+    # the stack's workspace plus prepared text rows for both prompts, the
+    # timestep path, the normalized image rows and two velocity buffers
+    extra = 2 * 160 * 3072 * 2 + 4 * 256 * 2 + (2 + 2 + 3 * 3 + 9 + 2) * 3072 * 2 \
+        + 4096 * 3072 * 2 + 2 * 4096 * 128 * 2
+    assert ns + extra <= n <= ns + extra + 20 * 256
+    assert sampler_ws(lib, model_desc(latent_ch=100))[0] == UNSUP
+    assert sampler_ws(lib, model_desc(text_dim=20))[0] == UNSUP
+    assert sampler_ws(lib, model_desc(latent_ch=0))[0] == SHAPE
+    assert sampler_ws(lib, model_desc(n_img=0))[0] == SHAPE
+
+
+def fake_weights(d, null=None, bad=None):
+    w = ops.ModelWeights()
+    addr = [P + (40 << 30)]
+
+    def nxt():
+        addr[0] += 1 << 28
+        return addr[0]
+    for name in ops.MODEL_TENSORS + ("out_mod_w", "out_mod_b", "out_w", "out_b"):
+        setattr(w, name, nxt())
+    for g in range(ops.N_GROUPS):
+        w.mod_w[g], w.mod_b[g] = nxt(), nxt()
+    st = d.stack
+    n = st.n_img_blocks + st.n_ref_blocks + st.n_txt_blocks + st.n_joint_blocks
+    arr = (ops.BlockWeights * max(n, 1))()
+    for i in range(n):
+        for name in ops.BLOCK_WEIGHTS:
+            setattr(arr[i], name, nxt())
+    w.blocks = arr
+    if null == "last_block":
+        arr[n - 1].k_scale = None
+    elif null is not None:
+        setattr(w, null, None)
+    if bad is not None:
+        setattr(w, bad, BAD)
+    return w, arr
+
+
+def prepare_call(lib, d, w, tc=P, tn=P + (1 << 30), ref=P + (2 << 30), pos=P + (3 << 30),
+                 wsp=P + (4 << 30), ws_bytes=None):
+    c = ctypes.c_void_p
+    if ws_bytes is None:
+        ws_bytes = sampler_ws(lib, d)[1]
+    return lib.dit_sampler_prepare(ctypes.byref(d), None if w is None else ctypes.byref(w),
+                                   c(tc) if tc else None, c(tn) if tn else None,
+                                   c(ref) if ref else None, c(pos) if pos else None,
+                                   c(wsp) if wsp else None, ctypes.c_size_t(ws_bytes), None)
+
+
+def step_call(lib, d, w, z=P, sigma=1.0, sigma_next=0.9, pos=P + (3 << 30), v=None,
+              wsp=P + (4 << 30), ws_bytes=None):
+    c = ctypes.c_void_p
+    if ws_bytes is None:
+        ws_bytes = sampler_ws(lib, d)[1]
+    return lib.dit_sampler_step(ctypes.byref(d), None if w is None else ctypes.byref(w),
+                                c(z) if z else None, sigma, sigma_next, c(pos) if pos else None,
+                                c(v) if v else None, c(wsp) if wsp else None,
+                                ctypes.c_size_t(ws_bytes), None)
+
+
+def test_sampler_host_errors(lib):
+    d = model_desc()
+    w, _keep = fake_weights(d)
+    small = sampler_ws(lib, d)[1] - 1
+    # every error is found before anything is launched
+    assert prepare_call(lib, d, None) == NULL
+    assert prepare_call(lib, d, w, tc=0) == NULL
+    assert prepare_call(lib, d, w, tn=0) == NULL           # guided: the negative prompt is needed
+    assert prepare_call(lib, d, w, tc=BAD) == ALIGN
+    assert prepare_call(lib, d, w, ws_bytes=small) == WS
+    # without references ref_latent, ref_in_* and the reference group may be null
+    w2, _k2 = fake_weights(d, null="ref_in_w")
+    w2.mod_w[1] = None
+    assert prepare_call(lib, d, w2, ref=0, ws_bytes=small) == WS
+    for name in ("img_in_w", "txt_in_b", "t_w2", "out_w", "out_mod_b", "last_block"):
+        wn, _kn = fake_weights(d, null=name)
+        assert prepare_call(lib, d, wn) == NULL, name
+        assert step_call(lib, d, wn) == NULL, name
+    wb, _kb = fake_weights(d, bad="t_b1")
+    assert step_call(lib, d, wb) == ALIGN
+    r = model_desc(n_ref=64, blocks=(1, 1, 1, 2))
+    wr, _kr = fake_weights(r, null="ref_in_b")
+    assert prepare_call(lib, r, wr) == NULL
+    wr, _kr = fake_weights(r)
+    assert prepare_call(lib, r, wr, ref=0) == NULL
+    assert step_call(lib, d, w, z=0) == NULL
+    assert step_call(lib, d, w, sigma=float("inf")) == ARG
+    assert step_call(lib, d, w, ws_bytes=small) == WS
+    assert step_call(lib, d, w, z=P + (4 << 30)) == ARG     # latent inside the workspace
+    assert step_call(lib, d, w, v=P) == ARG                 # velocity over the latent
+    assert step_call(lib, d, w, v=BAD) == ALIGN
+
+
+def test_linear_and_sinusoid_host_errors(lib):
+    c = ctypes.c_void_p
+    assert lib.dit_linear(4, 30, 16, c(P), c(P + (1 << 30)), None, 0, c(P + (2 << 30)), None) == UNSUP
+    assert lib.dit_linear(4, 32, 10, c(P), c(P + (1 << 30)), None, 0, c(P + (2 << 30)), None) == UNSUP
+    assert lib.dit_linear(-1, 32, 16, c(P), c(P + (1 << 30)), None, 0, c(P + (2 << 30)), None) == SHAPE
+    assert lib.dit_linear(4, 32, 16, c(P), c(P + (1 << 30)), None, 2, c(P + (2 << 30)), None) == ARG
+    assert lib.dit_linear(4, 32, 16, None, c(P + (1 << 30)), None, 0, c(P + (2 << 30)), None) == NULL
+    assert lib.dit_linear(4, 32, 16, c(BAD), c(P + (1 << 30)), None, 0, c(P + (2 << 30)), None) == ALIGN
+    assert lib.dit_linear(4, 32, 16, c(P), c(P + (1 << 30)), None, 0, c(P + 64), None) == ARG
+    assert lib.dit_linear(0, 32, 16, None, None, None, 0, None, None) == OK   # nothing to do
+    t = (ctypes.c_double * 2)(0.5, float("nan"))
+    assert lib.dit_time_sinusoid(0, t, c(P), None) == SHAPE
+    assert lib.dit_time_sinusoid(5, t, c(P), None) == SHAPE
+    assert lib.dit_time_sinusoid(2, t, c(P), None) == ARG
+    assert lib.dit_time_sinusoid(1, t, None, None) == NULL
+    assert lib.dit_time_sinusoid(1, t, c(BAD), None) == ALIGN

@@ -3,8 +3,10 @@
 Bounds.  The full block and attention bounds are the targets stated for this
 path: relative L2 <= 1e-2 for the block output y and for its branch r, and
 <= 5e-3 for attention alone.  AdaLN and RoPE have no stated bound; their only
-error is the final round to bf16 (at most 2^-9 relative per element, fp32
-arithmetic adds ~1e-6), so they are held to 2^-8 relative L2, twice that.
+error is the final round to bf16 (at most 2^-8 relative per element: half an
+ulp of an 8-bit significand) plus fp32 arithmetic (~1e-6), so they are held
+to 2^-8 + 1e-5 relative L2, which no mix of per-element errors within those
+bounds can exceed.
 Inputs are the seeded bf16 tensors shared with the oracle; sizes span several
 tiles and ragged tails, and the full-size configurations are checked on
 sampled rows the oracle evaluates one by one.
@@ -23,7 +25,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_BLOCK = 1e-2
 TOL_ATTN = 5e-3
-TOL_ROUND = 2.0 ** -8
+TOL_ROUND = 2.0 ** -8 + 1e-5
 
 
 @pytest.fixture(scope="module", autouse=True)

@@ -11,3 +11,6 @@ from .stack import cfg_combine, round_bf16, stack_branch, stack_cfg_ref  # noqa:
 from .sampler import (  # noqa: F401
     denoise_step, euler_cfg_step, flow_sigmas, linear, modulation, output_layers, sample,
     sampler_prepare, time_embedding, timestep_sinusoid)
+from .fp8 import (  # noqa: F401
+    block_ref_fp8, dequantize_rows, e4m3_decode, e4m3_round, e4m3_values, fp8_linear,
+    quantize_rows)

@@ -1,0 +1,139 @@
+"""Pins of the FP8 oracle (oracle/fp8.py): the e4m3 format from its
+definition, rounding against brute force and hand-worked encodings, the
+rowwise quantizer's invariants and error bound, exactness of the FP8 linear
+on exactly representable operands, and the FP8 block against the bf16 block
+within the quantization error."""
+import numpy as np
+import pytest
+
+import oracle
+
+DIMS = dict(n_heads=2, head_dim=8, mlp_hidden=24)
+D = 16
+
+
+def test_e4m3_table_from_the_format():
+    v = oracle.e4m3_values()
+    assert len(v) == 127 and np.all(np.diff(v) > 0)
+    assert v[0] == 0 and v[1] == 2.0 ** -9            # smallest subnormal: 1/8 * 2^-6
+    assert v[8] == 2.0 ** -6                           # smallest normal
+    assert v[126] == 448.0                             # 1.75 * 2^8, S.1111.110
+    assert v[0x38] == 1.0                              # exponent 7 = bias
+    # 8 values per binade, spaced 2^(e-3)
+    assert np.allclose(np.diff(v[0x38:0x41]), 1 / 8)
+    assert np.isnan(oracle.e4m3_decode([0x7F])[0]) and np.isnan(oracle.e4m3_decode([0xFF])[0])
+    assert oracle.e4m3_decode([0xFE])[0] == -448.0
+
+
+def nearest_bruteforce(x: float) -> int:
+    best, bd = None, None
+    for c in range(127):
+        val = oracle.e4m3_values()[c]
+        dd = abs(val - abs(x))
+        if bd is None or dd < bd or (dd == bd and c % 2 == 0):
+            best, bd = c, dd
+    return best | (0x80 if np.signbit(x) else 0)
+
+
+def test_e4m3_round_against_bruteforce():
+    v = oracle.e4m3_values()
+    rng = np.random.default_rng(0)
+    xs = np.concatenate([
+        rng.uniform(-448, 448, 1500),
+        rng.standard_normal(1500) * 2.0 ** rng.integers(-12, 6, 1500),
+        (v[:-1] + v[1:]) / 2,                          # every tie
+        -(v[:-1] + v[1:]) / 2,
+        v, -v])
+    xs = np.clip(xs, -448, 448)
+    got = oracle.e4m3_round(xs)
+    want = np.array([nearest_bruteforce(float(x)) for x in xs], dtype=np.uint8)
+    assert np.array_equal(got, want)
+
+
+def test_e4m3_hand_encodings():
+    cases = {1.0: 0x38, 1.0625: 0x38, 1.1875: 0x3A, 448.0: 0x7E, -448.0: 0xFE, 0.0: 0x00,
+             2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02, 0.75: 0x34, 3.0: 0x44, 240.0: 0x77,
+             232.0: 0x76, -1.0: 0xB8}
+    # 1.0625: tie between 1 (0x38) and 1.125 (0x39), to the even code
+    # 2^-10: tie between 0 and 2^-9; 3 * 2^-10: tie between 2^-9 and 2^-8 (0x02)
+    # 232: tie between 224 (0x76) and 240 (0x77); 0.75 = 1.5 * 2^-1: 0 0110 100
+    for x, c in cases.items():
+        assert oracle.e4m3_round([x])[0] == c, (x, hex(c))
+    with pytest.raises(ValueError):
+        oracle.e4m3_round([449.0])
+
+
+def test_quantize_rows_invariants_and_error_bound():
+    rng = np.random.default_rng(1)
+    x = oracle.round_bf16(rng.standard_normal((6, 64)) * np.array([1e-3, 0.1, 1, 10, 300, 1e4])[:, None])
+    x[2, :] = 0.0                                      # an all-zero row
+    q, s = oracle.quantize_rows(x)
+    assert q.dtype == np.uint8 and s.dtype == np.float32
+    assert s[2] == 0 and np.all(q[2] == 0)
+    for r in (0, 1, 3, 4, 5):
+        # the largest element maps to +-448 exactly
+        assert np.max(q[r] & 0x7F) == 0x7E
+        assert s[r] == np.float32(np.max(np.abs(x[r]))) / np.float32(448)
+    back = oracle.dequantize_rows(q, s)
+    # half a spacing of 3 mantissa bits (2^-4 relative) in the normal range,
+    # half the subnormal spacing (2^-10 s) below it, plus float32 steps
+    err = np.abs(back - x)
+    bound = 2.0 ** -4 * np.abs(x) + 2.0 ** -10 * s[:, None] + 1e-6 * np.abs(x)
+    assert np.all(err <= bound)
+
+
+def test_fp8_linear_is_exact_on_representable_operands():
+    # rows whose largest magnitude is exactly 448 * 2^k and whose entries are
+    # e4m3 values times 2^k quantize losslessly, so the FP8 product is exact
+    rng = np.random.default_rng(2)
+    v = oracle.e4m3_values()
+
+    def rows(n, k):
+        m = rng.choice(v, size=(n, k)) * rng.choice([-1, 1], size=(n, k))
+        m[:, 0] = 448.0
+        return m * 2.0 ** rng.integers(-8, 4, size=(n, 1))
+
+    a, w = rows(5, 32), rows(7, 32)
+    assert np.array_equal(oracle.fp8_linear(a, w), a @ w.T)
+    # a transposed scale (s_w on rows) would break this on unequal row scales
+    qa, sa = oracle.quantize_rows(a)
+    assert np.array_equal(oracle.dequantize_rows(qa, sa), a)
+
+
+def _block_inputs(seed=3, n=(12, 5)):
+    rng = np.random.default_rng(seed)
+    N, F = sum(n), DIMS["mlp_hidden"]
+    x = oracle.round_bf16(rng.standard_normal((N, D)))
+    mod = oracle.round_bf16(rng.standard_normal((len(n), 3, D)) * 0.3)
+    pos = np.zeros((N, 4), dtype=np.int64)
+    pos[:n[0], 1], pos[:n[0], 2] = np.arange(n[0]) // 4, np.arange(n[0]) % 4
+    pos[n[0]:, 0] = np.arange(n[1])
+    w_in = oracle.round_bf16(rng.standard_normal((3 * D + 2 * F, D)) / np.sqrt(D))
+    w_out = oracle.round_bf16(rng.standard_normal((D, D + F)) / np.sqrt(D + F))
+    g = np.ones(8)
+    return x, mod, pos, w_in, w_out, g, list(n)
+
+
+def test_fp8_block_tracks_the_bf16_block_within_quantization_error():
+    x, mod, pos, w_in, w_out, g, n = _block_inputs()
+    ref = oracle.block_ref(x, mod, pos, w_in, w_out, g, g, n, **DIMS, flags=3)["r"]
+    got = oracle.block_ref_fp8(x, mod, pos, w_in, w_out, g, g, n, **DIMS, flags=3)["r"]
+    e = oracle.rel_l2(got, ref)
+    # each FP8 operand carries about 2^-4 / sqrt(3) relative RMS error; two
+    # quantized products in series stay well under 0.15
+    assert 1e-3 < e < 0.15
+
+
+def test_fp8_block_rows_and_prequantized_weights_agree():
+    x, mod, pos, w_in, w_out, g, n = _block_inputs(seed=4)
+    full = oracle.block_ref_fp8(x, mod, pos, w_in, w_out, g, g, n, **DIMS)
+    rows = np.array([0, 5, 11, 12, 16])
+    part = oracle.block_ref_fp8(x, mod, pos, None, None, g, g, n, **DIMS, rows=rows,
+                                w_in_q=oracle.quantize_rows(w_in),
+                                w_out_q=oracle.quantize_rows(w_out))
+    assert np.allclose(part["y"], full["y"][rows], rtol=1e-12, atol=1e-12)
+    # a zero gate returns x exactly, as in the bf16 block
+    mod0 = mod.copy()
+    mod0[:, 2, :] = 0
+    assert np.array_equal(oracle.block_ref_fp8(x, mod0, pos, w_in, w_out, g, g, n, **DIMS)["y"],
+                          x)

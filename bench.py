@@ -13,7 +13,9 @@ the timed configuration.  A secondary field times one guided denoise step of
 the two-stage stack (c5) through dit_stack_fwd and the flow-matching sampler
 at the same shapes (`--no-stack` skips both), and
 another one block of the long 2048^2 editing sequence (2048^2 image, one
-2048^2 reference, 160 text tokens; `--no-long` skips it).
+2048^2 reference, 160 text tokens; `--no-long` skips it).  `block_fp8` times
+the same block with FP8 (rowwise e4m3) projections (`--no-fp8` skips it); it
+is a secondary line, not the bf16 metric.
 
 Prints one JSON line.
 """
@@ -33,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5033.2    # dense fp8 MFMA: twice the bf16 rate
 
 
 def parse():
@@ -45,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the secondary measurement of the two-stage stack with CFG (c5)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the secondary measurement of the block with FP8 projections")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the secondary measurement of the long editing sequence")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -230,6 +235,54 @@ def sampler_c5(torch, configs, ops, steps: int, warmup: int) -> dict:
         "ms_per_guided_step": round(step_ms, 3),
         "guided_50_step_transformer_s": round((prep_ms + 50 * step_ms) / 1e3, 3),
         "unguided_16_step_generation_s": round(gen16_s, 3),
+        "steps": steps, "warmup": warmup,
+    }
+
+
+def block_fp8(torch, configs, ops, timing, cfg, x, mod, pos, qs, ks, weights, steps: int,
+              warmup: int) -> dict:
+    """The same block (same inputs, the same rotating weight sets, quantized
+    rowwise to e4m3 once up front) through dit_block_fwd_fp8."""
+    D, F = cfg.width, cfg.mlp_hidden
+    wq = [(ops.quantize_rows_fp8(w_in), ops.quantize_rows_fp8(w_out)) for w_in, w_out in weights]
+    desc = ops.make_desc(cfg.n_tokens)
+    ws = ops.alloc_fp8_workspace(desc)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        (wi, si), (wo, so) = wq[i % len(wq)]
+        ops.block_fwd_fp8(x, mod, pos, wi, si, wo, so, qs, ks, desc, y=y, workspace=ws,
+                          stream=stream, events=events)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [timing.create(ops.N_STAGES + 1) for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    st = {name: float(np.mean([timing.elapsed_ms(e[j], e[j + 1]) for e in evs]))
+          for j, name in enumerate(ops.STAGES)}
+    for e in evs:
+        timing.destroy(e)
+    assert bool(torch.isfinite(y.float()).all())
+    gin = 2.0 * cfg.N * D * (3 * D + 2 * F)
+    gout = 2.0 * cfg.N * (D + F) * D
+    return {
+        "workload": f"{cfg.name} block with FP8 (rowwise e4m3) projections",
+        "dtype": "fp8 e4m3 projections, bf16 attention",
+        "ms_per_block": round(ms, 4),
+        "tflops": round(cfg.flop() / (ms * 1e-3) / 1e12, 2),
+        "stage_ms_mean": {k: round(v, 4) for k, v in st.items()},
+        "gemm_in_tflops": round(gin / (st["gemm_in"] * 1e-3) / 1e12, 2),
+        "gemm_in_frac_fp8_peak": round(gin / (st["gemm_in"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+        "gemm_out_with_quant_tflops": round(gout / (st["gemm_out"] * 1e-3) / 1e12, 2),
         "steps": steps, "warmup": warmup,
     }
 
@@ -432,6 +485,9 @@ def main():
 
     if not args.no_stack:
         result["stack_c5"] = stack_c5(torch, configs, ops, steps=3, warmup=1)
+    if not args.no_fp8:
+        result["block_fp8"] = block_fp8(torch, configs, ops, timing, cfg, x, mod, pos, qs, ks,
+                                        weights, args.steps, args.warmup)
     if not args.no_stack:
         result["sampler_c5"] = sampler_c5(torch, configs, ops, steps=3, warmup=1)
     if not args.no_long:

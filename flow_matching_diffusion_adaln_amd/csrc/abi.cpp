@@ -147,6 +147,88 @@ int block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const 
   return mark(DIT_N_STAGES);
 }
 
+// Workspace of the FP8 block: the bf16 block's, then the e4m3 codes and
+// rowwise scales of the two projections' inputs.
+struct WorkspaceF8 {
+  Workspace base;
+  uint8_t *u8, *cat8;
+  float *u_scale, *cat_scale;
+  size_t bytes;
+};
+
+WorkspaceF8 layout_fp8(const Shape& s, void* base) {
+  WorkspaceF8 w;
+  w.base = layout(s, base);
+  char* p = static_cast<char*>(base);
+  size_t off = w.base.bytes;
+  w.u8 = reinterpret_cast<uint8_t*>(p + off);
+  off += round_up((size_t)s.N * s.D);
+  w.cat8 = reinterpret_cast<uint8_t*>(p + off);
+  off += round_up((size_t)s.N * (s.D + s.F));
+  w.u_scale = reinterpret_cast<float*>(p + off);
+  off += round_up((size_t)s.N * 4);
+  w.cat_scale = reinterpret_cast<float*>(p + off);
+  off += round_up((size_t)s.N * 4);
+  w.bytes = off;
+  return w;
+}
+
+int block_fwd_fp8(const dit_block_desc* desc, const void* x, const void* mod, const int32_t* pos,
+                  const void* w_in8, const float* w_in_scale, const void* w_out8,
+                  const float* w_out_scale, const void* q_scale, const void* k_scale, void* y,
+                  void* workspace, size_t ws_bytes, hipStream_t stream, void* const* events) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc != DIT_OK) return rc;
+  if (s.N == 0) return DIT_OK;
+  if (!x || !mod || !pos || !w_in8 || !w_in_scale || !w_out8 || !w_out_scale || !q_scale ||
+      !k_scale || !y || !workspace)
+    return DIT_ERR_NULL;
+  if (misaligned(x) || misaligned(mod) || misaligned(pos) || misaligned(w_in8) ||
+      misaligned(w_in_scale) || misaligned(w_out8) || misaligned(w_out_scale) ||
+      misaligned(q_scale) || misaligned(k_scale) || misaligned(y) || misaligned(workspace))
+    return DIT_ERR_ALIGN;
+  const WorkspaceF8 w = layout_fp8(s, workspace);
+  if (ws_bytes < w.bytes) return DIT_ERR_WORKSPACE;
+  if (overlaps(y, (size_t)s.N * s.D * 2, workspace, w.bytes)) return DIT_ERR_ARG;
+  if (events) {
+    for (int i = 0; i <= DIT_N_STAGES; ++i)
+      if (!events[i]) return DIT_ERR_NULL;
+  }
+  auto mark = [&](int i) -> int {
+    if (!events) return DIT_OK;
+    return hip_status(hipEventRecord(static_cast<hipEvent_t>(events[i]), stream));
+  };
+  const Workspace& b = w.base;
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* mb = static_cast<const uint16_t*>(mod);
+  if ((rc = mark(DIT_STAGE_ADALN))) return rc;
+  if ((rc = hip_status(dit::launch_adaln_fp8(xb, mb, w.u8, w.u_scale, s.N, s.D, s.e0, s.e1,
+                                             desc->ln_eps, stream))))
+    return rc;
+  if ((rc = mark(DIT_STAGE_GEMM_IN))) return rc;
+  if ((rc = hip_status(dit::launch_gemm_in_fp8(
+           w.u8, w.u_scale, static_cast<const uint8_t*>(w_in8), w_in_scale, s.N, s.D, s.F, b.q,
+           b.k, b.v, b.cat, pos, static_cast<const uint16_t*>(q_scale),
+           static_cast<const uint16_t*>(k_scale), desc->rope_theta, desc->qk_eps, b.partial,
+           stream))))
+    return rc;
+  if ((rc = mark(DIT_STAGE_ROPE))) return rc;
+  if ((rc = mark(DIT_STAGE_ATTN))) return rc;
+  if ((rc = hip_status(dit::launch_attn(b.q, b.k, b.v, b.cat, s.N, s.H, s.D, s.D + s.F,
+                                        1.0f / sqrtf((float)DIT_HEAD_DIM), stream))))
+    return rc;
+  if ((rc = mark(DIT_STAGE_GEMM_OUT))) return rc;
+  // the output projection's input [o | m] is quantized rowwise first
+  if ((rc = hip_status(dit::launch_quant_rows(b.cat, w.cat8, w.cat_scale, s.N, s.D + s.F,
+                                              stream))) ||
+      (rc = hip_status(dit::launch_gemm_out_fp8(
+           w.cat8, w.cat_scale, static_cast<const uint8_t*>(w_out8), w_out_scale, s.N, s.D, s.F,
+           xb, mb, static_cast<uint16_t*>(y), s.e0, s.e1, desc->flags, b.partial, stream))))
+    return rc;
+  return mark(DIT_N_STAGES);
+}
+
 // Block descriptor of one stage of the stack: 1 stream of n tokens, or the
 // joint [image | reference | text] sequence (the reference segment only when
 // there are reference tokens).
@@ -705,6 +787,49 @@ int dit_time_sinusoid(int32_t n_t, const double* t, void* out, hipStream_t strea
     if (!isfinite(t[i])) return DIT_ERR_ARG;
   return hip_status(dit::launch_sinusoid(t, n_t, DIT_TIME_DIM, 1000.0, 10000.0,
                                          static_cast<uint16_t*>(out), stream));
+}
+
+int dit_quantize_rows_fp8(int32_t M, int32_t K, const void* x, void* q, float* scale,
+                          hipStream_t stream) {
+  if (M < 0 || K <= 0) return DIT_ERR_SHAPE;
+  if (K % 8 != 0) return DIT_ERR_UNSUPPORTED;
+  if ((long long)M * K * 2 >= kMaxBytes * 4) return DIT_ERR_UNSUPPORTED;
+  if (M == 0) return DIT_OK;
+  if (!x || !q || !scale) return DIT_ERR_NULL;
+  if (misaligned(x) || misaligned(q) || misaligned(scale)) return DIT_ERR_ALIGN;
+  const size_t xb = (size_t)M * K * 2, qb = (size_t)M * K, sb = (size_t)M * 4;
+  if (overlaps(q, qb, x, xb) || overlaps(scale, sb, x, xb) || overlaps(scale, sb, q, qb))
+    return DIT_ERR_ARG;
+  return hip_status(dit::launch_quant_rows(static_cast<const uint16_t*>(x),
+                                           static_cast<uint8_t*>(q), scale, M, K, stream));
+}
+
+int dit_block_fp8_workspace_bytes(const dit_block_desc* desc, size_t* bytes) {
+  Shape s;
+  const int rc = check_desc(desc, &s);
+  if (rc != DIT_OK) return rc;
+  if (!bytes) return DIT_ERR_NULL;
+  *bytes = layout_fp8(s, nullptr).bytes;
+  return DIT_OK;
+}
+
+int dit_block_fwd_fp8(const dit_block_desc* desc, const void* x, const void* mod,
+                      const int32_t* pos, const void* w_in8, const float* w_in_scale,
+                      const void* w_out8, const float* w_out_scale, const void* q_scale,
+                      const void* k_scale, void* y, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  return block_fwd_fp8(desc, x, mod, pos, w_in8, w_in_scale, w_out8, w_out_scale, q_scale,
+                       k_scale, y, workspace, workspace_bytes, stream, nullptr);
+}
+
+int dit_block_fwd_fp8_events(const dit_block_desc* desc, const void* x, const void* mod,
+                             const int32_t* pos, const void* w_in8, const float* w_in_scale,
+                             const void* w_out8, const float* w_out_scale, const void* q_scale,
+                             const void* k_scale, void* y, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream, void* const* events) {
+  if (!events) return DIT_ERR_NULL;
+  return block_fwd_fp8(desc, x, mod, pos, w_in8, w_in_scale, w_out8, w_out_scale, q_scale,
+                       k_scale, y, workspace, workspace_bytes, stream, events);
 }
 
 const char* dit_status_str(int status) {

@@ -9,15 +9,22 @@
 // owns one row; the row stays in registers (width / 64 values per lane) so the
 // two-pass statistics (mean, then the mean square deviation) cost no second
 // read.  Loads and stores are 16 bytes per lane and fully coalesced.
+//
+// FP8 variant: u is rounded to bf16 as above, then quantized rowwise to OCP
+// e4m3 with the row's scale (the same rule as quant.hip: inv = 448 / max|u|,
+// q = e4m3(clamp(u * inv)), s = max|u| / 448), and only the codes (1 byte per
+// element) and the scale are written: the FP8 input projection reads them.
 #include "common.h"
 #include "kernels.h"
 
 namespace dit {
 
-template <int CPL>  // 16-byte chunks per lane: width = 512 * CPL
+template <int CPL, bool F8>  // 16-byte chunks per lane: width = 512 * CPL
 __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t* __restrict__ x,
                                                     const uint16_t* __restrict__ mod,
-                                                    uint16_t* __restrict__ out, int n_rows,
+                                                    uint16_t* __restrict__ out,
+                                                    uint8_t* __restrict__ q8,
+                                                    float* __restrict__ q_scale, int n_rows,
                                                     int e0, int e1, float eps) {
   constexpr int W = 512 * CPL;
   const int lane = threadIdx.x & 63;
@@ -53,6 +60,7 @@ __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t* __restrict__
   const uint4* shift = reinterpret_cast<const uint4*>(mod + (size_t)st * 3 * W);
   const uint4* scale = reinterpret_cast<const uint4*>(mod + (size_t)st * 3 * W + W);
   uint4* orow = reinterpret_cast<uint4*>(out + (size_t)row * W);
+  uint4 ob[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const uint4 sh = shift[lane + 64 * i], sc = scale[lane + 64 * i];
@@ -66,18 +74,52 @@ __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t* __restrict__
       const float hi = (hi2f(w[t]) - mean) * rstd * (1.f + hi2f(b[t])) + hi2f(a[t]);
       o[t] = pack2(lo, hi);
     }
-    orow[lane + 64 * i] = make_uint4(o[0], o[1], o[2], o[3]);
+    ob[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    if constexpr (!F8) orow[lane + 64 * i] = ob[i];
+  }
+  if constexpr (F8) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const uint32_t w[4] = {ob[i].x, ob[i].y, ob[i].z, ob[i].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) m = fmaxf(m, fmaxf(fabsf(lo2f(w[t])), fabsf(hi2f(w[t]))));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float inv = m > 0.f ? 448.0f / m : 0.f;
+    if (lane == 0) q_scale[row] = m / 448.0f;
+    uint2* qrow = reinterpret_cast<uint2*>(q8 + (size_t)row * W);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const uint32_t w[4] = {ob[i].x, ob[i].y, ob[i].z, ob[i].w};
+      float f[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        f[2 * t] = fminf(fmaxf(lo2f(w[t]) * inv, -448.f), 448.f);
+        f[2 * t + 1] = fminf(fmaxf(hi2f(w[t]) * inv, -448.f), 448.f);
+      }
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+      qrow[lane + 64 * i] = make_uint2((uint32_t)lo, (uint32_t)hi);
+    }
   }
 }
 
-hipError_t launch_adaln(const uint16_t* x, const uint16_t* mod, uint16_t* out, int n_rows,
-                        int width, int e0, int e1, float eps, hipStream_t stream) {
+namespace {
+
+template <bool F8>
+hipError_t adaln_launch(const uint16_t* x, const uint16_t* mod, uint16_t* out, uint8_t* q8,
+                        float* q_scale, int n_rows, int width, int e0, int e1, float eps,
+                        hipStream_t stream) {
   const dim3 grid((n_rows + 3) / 4), block(256);
   switch (width / 512) {
-#define DIT_ADALN_CASE(C)                                                                   \
-  case C:                                                                                   \
-    hipLaunchKernelGGL(adaln_kernel<C>, grid, block, 0, stream, x, mod, out, n_rows, e0, e1, \
-                       eps);                                                                \
+#define DIT_ADALN_CASE(C)                                                                        \
+  case C:                                                                                        \
+    hipLaunchKernelGGL((adaln_kernel<C, F8>), grid, block, 0, stream, x, mod, out, q8, q_scale,  \
+                       n_rows, e0, e1, eps);                                                     \
     break;
     DIT_ADALN_CASE(1) DIT_ADALN_CASE(2) DIT_ADALN_CASE(3) DIT_ADALN_CASE(4)
     DIT_ADALN_CASE(5) DIT_ADALN_CASE(6) DIT_ADALN_CASE(7) DIT_ADALN_CASE(8)
@@ -88,6 +130,19 @@ hipError_t launch_adaln(const uint16_t* x, const uint16_t* mod, uint16_t* out, i
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_adaln(const uint16_t* x, const uint16_t* mod, uint16_t* out, int n_rows,
+                        int width, int e0, int e1, float eps, hipStream_t stream) {
+  return adaln_launch<false>(x, mod, out, nullptr, nullptr, n_rows, width, e0, e1, eps, stream);
+}
+
+hipError_t launch_adaln_fp8(const uint16_t* x, const uint16_t* mod, uint8_t* q8, float* q_scale,
+                            int n_rows, int width, int e0, int e1, float eps,
+                            hipStream_t stream) {
+  return adaln_launch<true>(x, mod, nullptr, q8, q_scale, n_rows, width, e0, e1, eps, stream);
 }
 
 }  // namespace dit

@@ -19,14 +19,24 @@
 // from v_mfma_f32_32x32x16_bf16 blocks with the fp32 accumulators in AGPRs.
 // The host picks the tile height: fewest rounds of tiles over the CUs, then
 // the shorter tile (224 divides the 4,256-token sequence into 19 tiles, 256
-// leaves a 160-row remainder).  The K loop streams 32-wide k
-// tiles from L2/HBM straight into LDS with 16-byte direct-to-LDS loads
-// through a 4-stage ring: loads run three tiles ahead of the MFMAs, which
-// hides the L2-miss latency that a double buffer exposes.  The 16-byte chunk
+// leaves a 160-row remainder).  The K loop streams k tiles of 128 bytes per
+// row (64 bf16) from L2/HBM straight into LDS with 16-byte direct-to-LDS
+// loads: W in a double buffer, A in a triple buffer when the K loop's period
+// allows it (loads of tile kt + 2 start during tile kt).  The 16-byte chunk
 // index is xor-swizzled by the row so fragment reads are bank-conflict free.
 // Tiles are ordered XCD-aware: each XCD takes one contiguous range of tiles,
 // walked in groups of 4 N-tiles so the A and W panels in flight on one XCD
-// stay few and L2-resident.
+// stay few.
+//
+// FP8 mode (F8): the same kernel on OCP e4m3 operands with rowwise scales,
+// the analogue of the rowwise-scaled FP8 ("fp8r") projections the SGLang
+// FLUX.3 page ships.  A k tile is then 128 one-byte elements: the same
+// 128-byte LDS rows, ring and swizzle, but 2 k steps of
+// v_mfma_scale_f32_32x32x64_f8f6f4 (64 k, unit block scale) instead of 4 of
+// the bf16 MFMA, so the MFMA time, LDS traffic and fragment reads per k tile
+// are unchanged and the k tile carries twice the FLOPs.  The accumulators
+// are multiplied by the A row's scale and the W row's scale before the
+// epilogue, which is otherwise the bf16 one.
 #include "common.h"
 #include "kernels.h"
 
@@ -36,7 +46,7 @@ namespace dit {
 
 namespace {
 
-constexpr int BN = 256, BK = 64;
+constexpr int BN = 256, BK = 64;  // BK in bf16 elements: 128 bytes per tile row
 constexpr int NW = 2;                // LDS slots for W k tiles (double buffer)
 constexpr int CH = BK / 8;           // 16-byte chunks per tile row (8 = one 128-byte cache line)
 constexpr int RPI = 64 / CH;         // tile rows filled by one 1 KB wave load (8)
@@ -75,7 +85,13 @@ struct GemmArgs {
   int n_dp, n_tail, n_pieces;
   int unit;           // k tiles per split unit (the K loop's unroll period)
   float* partial;     // 2 * n_pieces slots of BM * BN floats
+  int KT;             // k tiles of 128 bytes per row
+  // FP8 mode: A = q_a diag(s_a)^-1 row scales [M], W row scales [W rows]
+  const float* sa;
+  const float* sw;
 };
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Tile geometry: BM rows, WM x WN waves, MB x NB blocks of 32 x 32 per wave.
 template <int BM_>
@@ -307,6 +323,36 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g,
       }
 }
 
+// FP8 mode: multiplies a whole tile's accumulators by the rowwise scales,
+// s_a of the output row times s_w of the weight row of each column.
+template <int EPI, int BM>
+__device__ __forceinline__ void scale_acc(const GemmArgs& g,
+                                          f32x16 (&acc)[Tile<BM>::MB][Tile<BM>::NB], int tm,
+                                          int tn, int wm, int wn, int lane) {
+  constexpr int MB = Tile<BM>::MB, NB = Tile<BM>::NB;
+  const int ln = lane & 31, hl = lane >> 5;
+  float4 ws[NB][4];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      ws[j][rr] = *reinterpret_cast<const float4*>(
+          g.sw + weight_row<EPI, NB>(g, tn, (wn * NB + j) * 32 + 8 * rr + 4 * hl));
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const float sr = g.sa[min(tm * BM + (wm * MB + i) * 32 + ln, g.M - 1)];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        acc[i][j][4 * rr] *= sr * ws[j][rr].x;
+        acc[i][j][4 * rr + 1] *= sr * ws[j][rr].y;
+        acc[i][j][4 * rr + 2] *= sr * ws[j][rr].z;
+        acc[i][j][4 * rr + 3] *= sr * ws[j][rr].w;
+      }
+  }
+}
+
 // A partial tile in fp32: wave w's accumulators as consecutive 16-byte
 // groups, group-major, so each wave store / load moves 1 KB contiguously.
 template <int BM>
@@ -326,11 +372,14 @@ __device__ __forceinline__ int piece_start(int p, int units, int pieces) {
 // over them instead of bursting after the barrier; the K loop's unroll period
 // is then lcm(3, 2) = 6 k tiles.  NA = 2 serves K that is not a multiple of
 // 6 k tiles; then both operands load right after the barrier.
-template <int EPI, int BM, int NA>
+template <int EPI, int BM, int NA, bool F8>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   using T = Tile<BM>;
   constexpr int MB = T::MB, NB = T::NB;
   constexpr int PERIOD = NA == 3 ? 6 : 2;
+  constexpr int ES = F8 ? 1 : 2;    // bytes per element
+  constexpr int KSTEPS = F8 ? 2 : 4;  // MFMA k steps per k tile
+  using Frag = std::conditional_t<F8, i32x8, bf16x8>;
   // One LDS array per slot, not one indexed array: the compiler tracks
   // direct-to-LDS stores per LDS variable, so it can see that fragment reads
   // of one slot never alias the loads in flight into the others and does not
@@ -350,7 +399,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int ln = lane & 31, hl = lane >> 5;
 
-  const int KT = g.K / BK;      // a multiple of PERIOD (the host picks NA so)
+  const int KT = g.KT;          // a multiple of PERIOD (the host picks NA so)
   const int upt = KT / PERIOD;  // split units per tile
 
   // Work items: one whole tile, or the one or two tail tiles a split piece
@@ -381,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     uint32_t aoff[8], boff[8];
     static_assert(NLD_A <= 8 && NLD_B <= 8, "load offsets");
     f32x16 acc[MB][NB];
-    bf16x8 fa[2][MB], fb[2][NB];
+    Frag fa[2][MB], fb[2][NB];
     int tm, tn;
     tile_coords<BM>(g, id, tm, tn);
 
@@ -397,13 +446,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     for (int j = 0; j < NLD_A; ++j) {
       const int ra = (wave * NLD_A + j) * RPI + lrow;
       const int arow = min(tm * BM + ra, g.M - 1);
-      aoff[j] = ((uint32_t)arow * (uint32_t)g.K + (((lane % CH) ^ swz(ra)) * 8)) * 2u;
+      aoff[j] = (uint32_t)arow * (uint32_t)(g.K * ES) + (((lane % CH) ^ swz(ra)) * 16u);
     }
 #pragma unroll
     for (int j = 0; j < NLD_B; ++j) {
       const int rb = (wave * NLD_B + j) * RPI + lrow;
-      boff[j] = ((uint32_t)weight_row<EPI, NB>(g, tn, rb) * (uint32_t)g.K +
-                 (((lane % CH) ^ swz(rb)) * 8)) * 2u;
+      boff[j] = (uint32_t)weight_row<EPI, NB>(g, tn, rb) * (uint32_t)(g.K * ES) +
+                (((lane % CH) ^ swz(rb)) * 16u);
     }
     // Past k1 the last tile is reloaded into an idle slot (never read), so
     // the loop needs no branches.  gload_a issues A loads j0 .. j1 - 1 of k
@@ -431,18 +480,37 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // MFMA fragments, double-buffered in registers: while the MFMAs of one
-    // 16-wide k step run, the fragment reads of the next step are in flight.
+    // k step run, the next step's fragment reads are in flight.  A bf16
+    // fragment is the 16-byte chunk 2 ks + hl of the lane's row (8 k); an FP8
+    // fragment is chunks 4 ks + 2 hl and 4 ks + 2 hl + 1 (32 k): both operands
+    // use the same chunks, so the k order inside the MFMA does not matter.
+    auto lds16 = [&](const uint16_t* base, int r, int c) __attribute__((always_inline)) {
+      return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + r * 128 +
+                                             ((c ^ swz(r)) << 4));
+    };
     auto read_frags = [&](const uint16_t* sa, const uint16_t* sw, int ks, int slot)
                           __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         const int r = (wm * MB + i) * 32 + ln;
-        fa[slot][i] = *reinterpret_cast<const bf16x8*>(&sa[r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
+        if constexpr (F8) {
+          const uint4 x = lds16(sa, r, 4 * ks + 2 * hl), y = lds16(sa, r, 4 * ks + 2 * hl + 1);
+          fa[slot][i] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+                              (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        } else {
+          fa[slot][i] = __builtin_bit_cast(bf16x8, lds16(sa, r, 2 * ks + hl));
+        }
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int r = (wn * NB + j) * 32 + ln;
-        fb[slot][j] = *reinterpret_cast<const bf16x8*>(&sw[r * BK + (((2 * ks + hl) ^ swz(r)) << 3)]);
+        if constexpr (F8) {
+          const uint4 x = lds16(sw, r, 4 * ks + 2 * hl), y = lds16(sw, r, 4 * ks + 2 * hl + 1);
+          fb[slot][j] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+                              (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        } else {
+          fb[slot][j] = __builtin_bit_cast(bf16x8, lds16(sw, r, 2 * ks + hl));
+        }
       }
     };
     // C^T = W A^T: the weights are the A operand, so each lane ends up owning
@@ -451,11 +519,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[i][j] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NB; ++j) {
+          if constexpr (F8)
+            // formats 0 / 0: e4m3 for both operands; scale exponents 127: 2^0
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0, 127, 0, 127);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i],
+                                                                acc[i][j], 0, 0, 0);
+        }
     };
-    // One k tile (4 k steps of 16) from A slot i % NA and W slot i % 2, while
+    // One k tile (KSTEPS k steps) from A slot i % NA and W slot i % 2, while
     // tile kt + 1 lands in the other slots.  The instruction order is pinned
     // (the compiler would otherwise sink the loads next to the waits and pair
     // each fragment read with its first use).  Each k step's MFMAs run while
@@ -470,19 +544,24 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     auto ktile = [&](int kt, int i) __attribute__((always_inline)) {
       uint16_t* const sa = ring_a[i % NA];
       uint16_t* const sw = ring_w[i % NW];
+      constexpr int KS1 = KSTEPS - 1;  // k steps before the barrier
+      // one A load of tile kt + 2 after every GL_EVERY MFMAs: NLD_A of them
+      // fit in KS1 k steps of MB x NB MFMAs
+      constexpr int GL_EVERY = F8 ? 2 : 4;
 #pragma unroll
-      for (int ks = 0; ks < 3; ++ks) {
+      for (int ks = 0; ks < KS1; ++ks) {
         if constexpr (NA == 3) {
           // A loads of tile kt + 2: NLD_A split as evenly as possible
-          gload_a(kt + 2, ring_a[(i + 2) % 3], ks * NLD_A / 3, (ks + 1) * NLD_A / 3);
+          gload_a(kt + 2, ring_a[(i + 2) % 3], ks * NLD_A / KS1, (ks + 1) * NLD_A / KS1);
         }
         read_frags(sa, sw, ks + 1, (ks + 1) & 1);
         mfmas(ks & 1);
 #pragma unroll
         for (int q = 0; q < MB * NB; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-          if (NA == 3 && (q & 3) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+          if (NA == 3 && q % GL_EVERY == 1)
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+          __builtin_amdgcn_sched_group_barrier(0x100, F8 ? 2 : 1, 0);  // LDS reads
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -494,12 +573,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
       if constexpr (NA == 2) gload_a(kt + 2, sa, 0, NLD_A);
       gload_w(kt + 2, sw);
       read_frags(ring_a[(i + 1) % NA], ring_w[(i + 1) % NW], 0, 0);
-      mfmas(1);
+      mfmas(KS1 & 1);
 #pragma unroll
       for (int q = 0; q < MB * NB; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global load
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+        __builtin_amdgcn_sched_group_barrier(0x100, F8 ? 2 : 1, 0);  // LDS reads
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -519,6 +598,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
     if constexpr (!SPLIT) {
+      if constexpr (F8) scale_acc<EPI, BM>(g, acc, tm, tn, wm, wn, lane);
       epilogue<EPI, BM>(g, acc, tm, tn, wm, wn, lane);
     } else {
       float4* dst = partial_slot<BM>(g, slot, wave, lane);
@@ -553,7 +633,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 // 16-byte accumulator groups (blocks 2 jp and 2 jp + 1 of one wave, one rr,
 // one lane), so each wave load reads 1 KB contiguously and every thread has
 // two independent loads per partial in flight.
-template <int EPI, int BM>
+template <int EPI, int BM, bool F8>
 __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
   using T = Tile<BM>;
   constexpr int MB = T::MB, NB = T::NB;
@@ -572,7 +652,7 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
   const int wm = wave / T::WN, wn = wave % T::WN;
   int tm, tn;
   tile_coords<BM>(g, g.n_dp + t_rel, tm, tn);
-  const int upt = g.K / BK / g.unit;
+  const int upt = g.KT / g.unit;
   const int units = g.n_tail * upt;
   const int ua = t_rel * upt, ub = ua + upt;  // this tile's units
   // first and last pieces that touch the tile
@@ -592,6 +672,15 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
     const float4 va = src[g0], vb = src[g1];
     a[0] += va.x; a[1] += va.y; a[2] += va.z; a[3] += va.w;
     b[0] += vb.x; b[1] += vb.y; b[2] += vb.z; b[3] += vb.w;
+  }
+  if constexpr (F8) {
+    const int ln = lane & 31, hl = lane >> 5;
+    const float sr = g.sa[min(tm * BM + (wm * MB + i) * 32 + ln, g.M - 1)];
+    const int r0 = (wn * NB + 2 * jp) * 32 + 8 * rr + 4 * hl;
+    const float4 wa = *reinterpret_cast<const float4*>(g.sw + weight_row<EPI, NB>(g, tn, r0));
+    const float4 wb = *reinterpret_cast<const float4*>(g.sw + weight_row<EPI, NB>(g, tn, r0 + 32));
+    a[0] *= sr * wa.x; a[1] *= sr * wa.y; a[2] *= sr * wa.z; a[3] *= sr * wa.w;
+    b[0] *= sr * wb.x; b[1] *= sr * wb.y; b[2] *= sr * wb.z; b[3] *= sr * wb.w;
   }
   epilogue_pair<EPI, BM>(g, tm, tn, wm, wn, lane, i, jp, rr, a, b);
 }
@@ -619,20 +708,20 @@ int device_cus() {
 // fp32 partials in K order and runs the epilogue.
 // K loop unroll period in k tiles: 6 (3 A slots) when it divides K / BK,
 // else 2 (K is a multiple of 128 for every supported shape).
-int unroll_period(int K) { return (K / BK) % 6 == 0 ? 6 : 2; }
+int unroll_period(int KT) { return KT % 6 == 0 ? 6 : 2; }
 
 struct Plan {
   int bm, tiles, n_dp, n_tail, n_pieces;
   float cost;  // estimated time in tile times
 };
 
-Plan make_plan(int bm, int M, int K, int num_n, bool can_split) {
+Plan make_plan(int bm, int M, int KT, int num_n, bool can_split) {
   const int cus = device_cus();
   Plan p{};
   p.bm = bm;
   p.tiles = ((M + bm - 1) / bm) * num_n;
   const int full = p.tiles / cus, tail = p.tiles - full * cus;
-  const int upt = K / BK / unroll_period(K);
+  const int upt = KT / unroll_period(KT);
   // a 224-row tile takes about as long as a 256-row one (the k loop's fixed
   // per-step latency dominates), so cost is counted in tiles
   const float tile_time = 1.0f;
@@ -657,49 +746,50 @@ Plan make_plan(int bm, int M, int K, int num_n, bool can_split) {
 // (4,256 tokens x 12 output tiles: 228 tiles in one round, where 256-row tiles
 // need 204 but each is slower); the cheaper plan wins, ties going to the
 // shorter tile.
-Plan pick_plan(int M, int K, int num_n, bool can_split) {
-  const Plan a = make_plan(224, M, K, num_n, can_split);
-  const Plan b = make_plan(256, M, K, num_n, can_split);
+Plan pick_plan(int M, int KT, int num_n, bool can_split) {
+  const Plan a = make_plan(224, M, KT, num_n, can_split);
+  const Plan b = make_plan(256, M, KT, num_n, can_split);
   return a.cost <= b.cost ? a : b;
 }
 
-template <int EPI>
+template <int EPI, bool F8>
 hipError_t launch(GemmArgs g, hipStream_t stream) {
   const bool can_split = g.partial != nullptr;
+  g.KT = g.K * (F8 ? 1 : 2) / 128;
   Plan p;
   if constexpr (EPI == EPI_IN) {
     // 256-row tiles only: the q / k epilogue needs a whole head per wave.
     // Split tail tiles end in the fix-up kernel, whose epilogue does not
     // normalize or rotate, so a tail must hold no q or k tile (tail tiles are
     // the last in tile order, i.e. the highest N tiles: MLP ones).
-    p = make_plan(256, g.M, g.K, g.num_n, can_split);
+    p = make_plan(256, g.M, g.KT, g.num_n, can_split);
     const int num_m = (g.M + 255) / 256;
     if (p.n_tail && (p.n_dp / (GROUP_N * num_m)) * GROUP_N < 2 * g.D / BN)
-      p = make_plan(256, g.M, g.K, g.num_n, false);
+      p = make_plan(256, g.M, g.KT, g.num_n, false);
   } else {
-    p = pick_plan(g.M, g.K, g.num_n, can_split);
+    p = pick_plan(g.M, g.KT, g.num_n, can_split);
   }
   g.n_dp = p.n_dp;
   g.n_tail = p.n_tail;
   g.n_pieces = p.n_pieces;
-  g.unit = unroll_period(g.K);
+  g.unit = unroll_period(g.KT);
   const int grid = g.n_dp + (g.n_tail ? g.n_pieces : 0);
   const bool tall = EPI == EPI_IN || p.bm == 256;
   if (tall) {
     if (g.unit == 6)
-      hipLaunchKernelGGL((gemm_kernel<EPI, 256, 3>), dim3(grid), dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((gemm_kernel<EPI, 256, 3, F8>), dim3(grid), dim3(256), 0, stream, g);
     else
-      hipLaunchKernelGGL((gemm_kernel<EPI, 256, 2>), dim3(grid), dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((gemm_kernel<EPI, 256, 2, F8>), dim3(grid), dim3(256), 0, stream, g);
     if (g.n_tail)
-      hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 256>), dim3(g.n_tail * 256 * BN / 8 / 256),
+      hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 256, F8>), dim3(g.n_tail * 256 * BN / 8 / 256),
                          dim3(256), 0, stream, g);
   } else if constexpr (EPI == EPI_OUT) {
     if (g.unit == 6)
-      hipLaunchKernelGGL((gemm_kernel<EPI, 224, 3>), dim3(grid), dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((gemm_kernel<EPI, 224, 3, F8>), dim3(grid), dim3(256), 0, stream, g);
     else
-      hipLaunchKernelGGL((gemm_kernel<EPI, 224, 2>), dim3(grid), dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((gemm_kernel<EPI, 224, 2, F8>), dim3(grid), dim3(256), 0, stream, g);
     if (g.n_tail)
-      hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 224>), dim3(g.n_tail * 224 * BN / 8 / 256),
+      hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 224, F8>), dim3(g.n_tail * 224 * BN / 8 / 256),
                          dim3(256), 0, stream, g);
   }
   return hipGetLastError();
@@ -707,10 +797,11 @@ hipError_t launch(GemmArgs g, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D, int F,
-                          uint16_t* q, uint16_t* k, uint16_t* v, uint16_t* cat,
-                          const int32_t* pos, const uint16_t* q_scale, const uint16_t* k_scale,
-                          float theta, float qk_eps, float* partial, hipStream_t stream) {
+namespace {
+
+GemmArgs in_args(const void* u, const void* w_in, int M, int D, int F, uint16_t* q, uint16_t* k,
+                 uint16_t* v, uint16_t* cat, const int32_t* pos, const uint16_t* q_scale,
+                 const uint16_t* k_scale, float theta, float qk_eps, float* partial) {
   GemmArgs g{};
   g.pos = pos;
   g.q_scale = q_scale;
@@ -719,8 +810,8 @@ hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D,
   const double two_pi = 6.283185307179586;
   for (int j = 0; j < 16; ++j) g.rope_rev[j] = pow((double)theta, -2.0 * j / 32.0) / two_pi;
   g.partial = partial;
-  g.A = u;
-  g.W = w_in;
+  g.A = static_cast<const uint16_t*>(u);
+  g.W = static_cast<const uint16_t*>(w_in);
   g.M = M;
   g.K = D;
   g.num_n = 3 * D / BN + F / 128;
@@ -730,16 +821,16 @@ hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D,
   g.k = k;
   g.v = v;
   g.cat = cat;
-  return launch<EPI_IN>(g, stream);
+  return g;
 }
 
-hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, int D, int F,
-                           const uint16_t* x, const uint16_t* mod, uint16_t* y, int e0, int e1,
-                           uint32_t flags, float* partial, hipStream_t stream) {
+GemmArgs out_args(const void* cat, const void* w_out, int M, int D, int F, const uint16_t* x,
+                  const uint16_t* mod, uint16_t* y, int e0, int e1, uint32_t flags,
+                  float* partial) {
   GemmArgs g{};
   g.partial = partial;
-  g.A = cat;
-  g.W = w_out;
+  g.A = static_cast<const uint16_t*>(cat);
+  g.W = static_cast<const uint16_t*>(w_out);
   g.M = M;
   g.K = D + F;
   g.num_n = D / BN;
@@ -751,7 +842,48 @@ hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, in
   g.e0 = e0;
   g.e1 = e1;
   g.flags = flags;
-  return launch<EPI_OUT>(g, stream);
+  return g;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D, int F,
+                          uint16_t* q, uint16_t* k, uint16_t* v, uint16_t* cat,
+                          const int32_t* pos, const uint16_t* q_scale, const uint16_t* k_scale,
+                          float theta, float qk_eps, float* partial, hipStream_t stream) {
+  return launch<EPI_IN, false>(in_args(u, w_in, M, D, F, q, k, v, cat, pos, q_scale, k_scale,
+                                       theta, qk_eps, partial),
+                               stream);
+}
+
+hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, int D, int F,
+                           const uint16_t* x, const uint16_t* mod, uint16_t* y, int e0, int e1,
+                           uint32_t flags, float* partial, hipStream_t stream) {
+  return launch<EPI_OUT, false>(out_args(cat, w_out, M, D, F, x, mod, y, e0, e1, flags, partial),
+                                stream);
+}
+
+hipError_t launch_gemm_in_fp8(const uint8_t* u8, const float* u_scale, const uint8_t* w_in8,
+                              const float* w_in_scale, int M, int D, int F, uint16_t* q,
+                              uint16_t* k, uint16_t* v, uint16_t* cat, const int32_t* pos,
+                              const uint16_t* q_scale, const uint16_t* k_scale, float theta,
+                              float qk_eps, float* partial, hipStream_t stream) {
+  GemmArgs g = in_args(u8, w_in8, M, D, F, q, k, v, cat, pos, q_scale, k_scale, theta, qk_eps,
+                       partial);
+  g.sa = u_scale;
+  g.sw = w_in_scale;
+  return launch<EPI_IN, true>(g, stream);
+}
+
+hipError_t launch_gemm_out_fp8(const uint8_t* cat8, const float* cat_scale,
+                               const uint8_t* w_out8, const float* w_out_scale, int M, int D,
+                               int F, const uint16_t* x, const uint16_t* mod, uint16_t* y,
+                               int e0, int e1, uint32_t flags, float* partial,
+                               hipStream_t stream) {
+  GemmArgs g = out_args(cat8, w_out8, M, D, F, x, mod, y, e0, e1, flags, partial);
+  g.sa = cat_scale;
+  g.sw = w_out_scale;
+  return launch<EPI_OUT, true>(g, stream);
 }
 
 }  // namespace dit

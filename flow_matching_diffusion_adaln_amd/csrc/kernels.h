@@ -16,6 +16,17 @@ constexpr size_t kGemmPartialBytes = (size_t)2 * GEMM_MAX_SPLIT_PIECES * 256 * 2
 hipError_t launch_adaln(const uint16_t* x, const uint16_t* mod, uint16_t* out, int n_rows,
                         int width, int e0, int e1, float eps, hipStream_t stream);
 
+// FP8 variant: u rounded to bf16, then quantized rowwise to e4m3 codes q8
+// [n_rows, width] with one float scale per row (u ~ q8 * q_scale).
+hipError_t launch_adaln_fp8(const uint16_t* x, const uint16_t* mod, uint8_t* q8, float* q_scale,
+                            int n_rows, int width, int e0, int e1, float eps,
+                            hipStream_t stream);
+
+// Rowwise e4m3 quantization of bf16 x [M, K] (K a multiple of 8): codes q
+// [M, K], scales [M] with x ~ q * scale.
+hipError_t launch_quant_rows(const uint16_t* x, uint8_t* q, float* scale, int M, int K,
+                             hipStream_t stream);
+
 hipError_t launch_rope4(uint16_t* q, uint16_t* k, const int32_t* pos, const uint16_t* q_scale,
                         const uint16_t* k_scale, int n_tokens, int n_heads, float theta,
                         float eps, hipStream_t stream);
@@ -32,6 +43,20 @@ hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D,
 hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, int D, int F,
                            const uint16_t* x, const uint16_t* mod, uint16_t* y, int e0, int e1,
                            uint32_t flags, float* partial, hipStream_t stream);
+
+// FP8 projections: e4m3 operands with rowwise scales (u8 / cat8 rows scaled
+// by u_scale / cat_scale, weight rows by w_*_scale), epilogues as above.
+hipError_t launch_gemm_in_fp8(const uint8_t* u8, const float* u_scale, const uint8_t* w_in8,
+                              const float* w_in_scale, int M, int D, int F, uint16_t* q,
+                              uint16_t* k, uint16_t* v, uint16_t* cat, const int32_t* pos,
+                              const uint16_t* q_scale, const uint16_t* k_scale, float theta,
+                              float qk_eps, float* partial, hipStream_t stream);
+
+hipError_t launch_gemm_out_fp8(const uint8_t* cat8, const float* cat_scale,
+                               const uint8_t* w_out8, const float* w_out_scale, int M, int D,
+                               int F, const uint16_t* x, const uint16_t* mod, uint16_t* y,
+                               int e0, int e1, uint32_t flags, float* partial,
+                               hipStream_t stream);
 
 // out = neg + scale * (cond - neg) elementwise over n bf16 values (n a multiple of 8)
 hipError_t launch_cfg_combine(const uint16_t* cond, const uint16_t* neg, uint16_t* out,

@@ -25,7 +25,9 @@ STAGES = ("adaln", "gemm_in", "rope", "attn", "gemm_out")
 EXPORTS = ("dit_block_workspace_bytes", "dit_block_fwd", "dit_block_fwd_events", "dit_attn_fwd",
            "rope4_apply", "adaln_mod", "dit_stack_workspace_bytes", "dit_stack_fwd",
            "dit_flow_sigmas", "dit_sampler_workspace_bytes", "dit_sampler_prepare",
-           "dit_sampler_step", "dit_linear", "dit_time_sinusoid", "dit_status_str")
+           "dit_sampler_step", "dit_linear", "dit_time_sinusoid", "dit_quantize_rows_fp8",
+           "dit_block_fp8_workspace_bytes", "dit_block_fwd_fp8", "dit_block_fwd_fp8_events",
+           "dit_status_str")
 N_GROUPS = 4        # block groups with their own modulation: stage-1 image, reference, text; joint
 TIME_DIM = 256
 
@@ -122,6 +124,11 @@ def load_library() -> ctypes.CDLL:
     lib.dit_sampler_step.argtypes = [model_p, weights_p, vp, f64, f64, vp, vp, vp, sz, vp]
     lib.dit_linear.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp]
     lib.dit_time_sinusoid.argtypes = [i32, ctypes.POINTER(f64), vp, vp]
+    lib.dit_quantize_rows_fp8.argtypes = [i32, i32, vp, vp, vp, vp]
+    lib.dit_block_fp8_workspace_bytes.argtypes = [desc_p, ctypes.POINTER(sz)]
+    lib.dit_block_fwd_fp8.argtypes = [desc_p] + [vp] * 10 + [vp, sz, vp]
+    lib.dit_block_fwd_fp8_events.argtypes = [desc_p] + [vp] * 10 + [vp, sz, vp,
+                                                                   ctypes.POINTER(vp)]
     lib.dit_status_str.argtypes = [ctypes.c_int]
     lib.dit_status_str.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -479,3 +486,70 @@ def time_sinusoid(ts, out=None, stream=None) -> torch.Tensor:
         out = torch.empty((n, TIME_DIM), dtype=torch.bfloat16, device="cuda")
     _check(load_library().dit_time_sinusoid(n, arr, _ptr(out), _stream(stream)))
     return out
+
+
+# ---- FP8 projections ---------------------------------------------------------------
+
+def quantize_rows_fp8(x, q=None, scale=None, stream=None):
+    """(codes uint8 [M, K], scales float32 [M]) of bf16 x [M, K] (dit_quantize_rows_fp8)."""
+    M, K = x.shape
+    _bf16(x, (M, K), "x")
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    if q.dtype != torch.uint8 or tuple(q.shape) != (M, K) or not q.is_contiguous():
+        raise ValueError("q must be a contiguous uint8 [M, K] tensor")
+    if scale.dtype != torch.float32 or tuple(scale.shape) != (M,):
+        raise ValueError("scale must be a float32 [M] tensor")
+    _check(load_library().dit_quantize_rows_fp8(M, K, _ptr(x), _ptr(q), _ptr(scale),
+                                                _stream(stream)))
+    return q, scale
+
+
+def block_fp8_workspace_bytes(desc: BlockDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().dit_block_fp8_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def alloc_fp8_workspace(desc: BlockDesc, device="cuda") -> torch.Tensor:
+    return torch.empty(max(block_fp8_workspace_bytes(desc), 1), dtype=torch.uint8, device=device)
+
+
+def _fp8_weight(q, s, shape, name):
+    if q.dtype != torch.uint8 or tuple(q.shape) != tuple(shape) or not q.is_cuda \
+            or not q.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous uint8 {tuple(shape)} GPU tensor")
+    if s.dtype != torch.float32 or tuple(s.shape) != (shape[0],) or not s.is_contiguous():
+        raise ValueError(f"{name} scales must be a contiguous float32 [{shape[0]}] tensor")
+
+
+def block_fwd_fp8(x, mod, pos, w_in8, w_in_scale, w_out8, w_out_scale, q_scale, k_scale,
+                  desc: BlockDesc, y=None, workspace=None, stream=None, events=None):
+    """y = dit_block_fwd_fp8(...): the block with FP8 projections; the weights
+    as returned by quantize_rows_fp8."""
+    N = sum(desc.n_tokens[i] for i in range(desc.n_streams))
+    D, F, d = desc.width, desc.mlp_hidden, desc.head_dim
+    _bf16(x, (N, D), "x")
+    _bf16(mod, (desc.n_streams, 3, D), "mod")
+    _pos_check(pos, N)
+    _fp8_weight(w_in8, w_in_scale, (3 * D + 2 * F, D), "w_in8")
+    _fp8_weight(w_out8, w_out_scale, (D, D + F), "w_out8")
+    _bf16(q_scale, (d,), "q_scale")
+    _bf16(k_scale, (d,), "k_scale")
+    if y is None:
+        y = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_fp8_workspace(desc, x.device)
+    args = [ctypes.byref(desc), _ptr(x), _ptr(mod), ctypes.c_void_p(pos.data_ptr()),
+            _ptr(w_in8), _ptr(w_in_scale), _ptr(w_out8), _ptr(w_out_scale), _ptr(q_scale),
+            _ptr(k_scale), _ptr(y), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+            _stream(stream)]
+    lib = load_library()
+    if events is None:
+        _check(lib.dit_block_fwd_fp8(*args))
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        _check(lib.dit_block_fwd_fp8_events(*args, arr))
+    return y

@@ -151,6 +151,50 @@ int rope4_apply(int32_t n_tokens, int32_t n_heads, int32_t head_dim, void* q, vo
 int adaln_mod(int32_t n_streams, const int32_t* n_tokens, int32_t width, const void* x,
               const void* mod, void* out, float eps, hipStream_t stream);
 
+/* ---- FP8 projections (rowwise-scaled e4m3) ---------------------------------
+ * The analogue of the rowwise-scaled FP8 linear layers ("fp8r") that the
+ * SGLang FLUX.3 page ships for latency, on gfx950's FP8 MFMA (OCP e4m3).
+ * Rowwise quantization of a bf16 matrix X [M, K], per row r:
+ *   a_r = max_k |x_rk|, inv_r = 448 / a_r and s_r = a_r / 448 (float32,
+ *   correctly rounded), q_rk = e4m3(clamp(x_rk * inv_r, -448, 448)) rounded
+ *   to nearest even, so x_rk ~ q_rk * s_r; an all-zero row gets s_r = 0 and
+ *   q = 0.
+ * The FP8 block is dit_block_fwd with both projections in FP8: u (the AdaLN
+ * output, rounded to bf16) and [o | m] are quantized per token row, W_in and
+ * W_out per output row (once, with dit_quantize_rows_fp8), and each product
+ * is sum_k q_a q_w * s_a s_w with fp32 accumulation.  Everything else (the
+ * QK norm, RoPE, attention, SwiGLU, gate and residual) is as in the bf16 block. */
+
+/* Rowwise quantization: x bf16 [M, K] -> q e4m3 [M, K] (1 byte each), scale
+ * float [M].  K a multiple of 8.  Device pointers, 16-byte aligned, not
+ * overlapping. */
+int dit_quantize_rows_fp8(int32_t M, int32_t K, const void* x, void* q, float* scale,
+                          hipStream_t stream);
+
+/* Bytes of device workspace dit_block_fwd_fp8 needs: the bf16 block's plus
+ * the codes and scales of u and [o | m]. */
+int dit_block_fp8_workspace_bytes(const dit_block_desc* desc, size_t* bytes);
+
+/* The block with FP8 projections.  Arguments as dit_block_fwd, except:
+ *   w_in8       e4m3 [3D + 2F, D]  and w_in_scale  float [3D + 2F]
+ *   w_out8      e4m3 [D, D + F]    and w_out_scale float [D]
+ * as produced by dit_quantize_rows_fp8 from the bf16 weights.  Errors as for
+ * dit_block_fwd. */
+int dit_block_fwd_fp8(const dit_block_desc* desc, const void* x, const void* mod,
+                      const int32_t* pos, const void* w_in8, const float* w_in_scale,
+                      const void* w_out8, const float* w_out_scale, const void* q_scale,
+                      const void* k_scale, void* y, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* dit_block_fwd_fp8 with DIT_N_STAGES + 1 events recorded between its stages
+ * (as dit_block_fwd_events; the quantization of [o | m] is in the output
+ * projection's stage). */
+int dit_block_fwd_fp8_events(const dit_block_desc* desc, const void* x, const void* mod,
+                             const int32_t* pos, const void* w_in8, const float* w_in_scale,
+                             const void* w_out8, const float* w_out_scale, const void* q_scale,
+                             const void* k_scale, void* y, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream, void* const* events);
+
 /* ---- Two-stage stack and classifier-free guidance -------------------------
  * One denoise step of the transformer ("Welcome FLUX.3 Image Klein in
  * Diffusers", section "How it works": each stream, text, image and

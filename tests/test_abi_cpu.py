@@ -410,3 +410,53 @@ def test_linear_and_sinusoid_host_errors(lib):
     assert lib.dit_time_sinusoid(2, t, c(P), None) == ARG
     assert lib.dit_time_sinusoid(1, t, None, None) == NULL
     assert lib.dit_time_sinusoid(1, t, c(BAD), None) == ALIGN
+
+
+# ---- FP8 projections ---------------------------------------------------------------
+
+def test_fp8_workspace_bytes(lib):
+    d = ops.make_desc([4096, 160])
+    n = ctypes.c_size_t(0)
+    assert lib.dit_block_fp8_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == OK
+    _, nb = ws(lib, d)
+    # the bf16 block's workspace plus u and [o | m] in e4m3 and their row scales
+    extra = 4256 * 3072 + 4256 * (3072 + 9216) + 2 * 4256 * 4
+    assert nb + extra <= n.value <= nb + extra + 4 * 256
+    assert lib.dit_block_fp8_workspace_bytes(None, ctypes.byref(n)) == NULL
+
+
+def fp8_call(lib, d, ptrs=None, ws_bytes=None):
+    p = [P + (i << 30) for i in range(11)] if ptrs is None else ptrs
+    if ws_bytes is None:
+        n = ctypes.c_size_t(0)
+        lib.dit_block_fp8_workspace_bytes(ctypes.byref(d), ctypes.byref(n))
+        ws_bytes = n.value
+    c = [ctypes.c_void_p(v) if v else None for v in p]
+    return lib.dit_block_fwd_fp8(ctypes.byref(d), *c[:10], c[10], ctypes.c_size_t(ws_bytes),
+                                 None)
+
+
+def test_fp8_host_errors(lib):
+    d = ops.make_desc([256, 80])
+    good = [P + (i << 30) for i in range(11)]
+    for i in range(11):  # x, mod, pos, w_in8, w_in_scale, w_out8, w_out_scale, q/k scale, y, ws
+        bad = list(good)
+        bad[i] = 0
+        assert fp8_call(lib, d, bad) == NULL, i
+        bad[i] = BAD
+        assert fp8_call(lib, d, bad) == ALIGN, i
+    n = ctypes.c_size_t(0)
+    lib.dit_block_fp8_workspace_bytes(ctypes.byref(d), ctypes.byref(n))
+    assert fp8_call(lib, d, ws_bytes=n.value - 1) == WS
+    over = list(good)
+    over[9] = good[10]                                   # y inside the workspace
+    assert fp8_call(lib, d, over) == ARG
+    assert fp8_call(lib, ops.make_desc([256, 80], width=3000)) == SHAPE
+    assert fp8_call(lib, ops.make_desc([0])) == OK       # nothing to do
+    c = ctypes.c_void_p
+    assert lib.dit_quantize_rows_fp8(4, 12, c(P), c(P + (1 << 30)), c(P + (2 << 30)), None) == UNSUP
+    assert lib.dit_quantize_rows_fp8(-1, 16, c(P), c(P + (1 << 30)), c(P + (2 << 30)), None) == SHAPE
+    assert lib.dit_quantize_rows_fp8(4, 16, None, c(P + (1 << 30)), c(P + (2 << 30)), None) == NULL
+    assert lib.dit_quantize_rows_fp8(4, 16, c(P), c(BAD), c(P + (2 << 30)), None) == ALIGN
+    assert lib.dit_quantize_rows_fp8(4, 16, c(P), c(P + 64), c(P + (2 << 30)), None) == ARG
+    assert lib.dit_quantize_rows_fp8(0, 16, None, None, None, None) == OK

@@ -163,8 +163,8 @@ def test_block_parity_single_token():
 
 # On a 256-CU device these token counts make the GEMMs cut their last, partly
 # filled round of tiles along K (fp32 partial tiles + a fix-up pass):
-#   513:   input projection, 224-row tiles, 1 round + 68 tiles
-#   700:   input projection, 256-row tiles, 1 round + 68 tiles
+#   513:   input projection (3 x 108 tiles of 256 rows), 1 round + 68 tiles
+#   700:   input projection, likewise 1 round + 68 tiles
 #   4,256: input projection, 256-row tiles, 7 rounds + 44 tiles (the 1024^2
 #          workload, covered by the c2 tests)
 #   5,601: both projections, 256-row tiles (output: 1 round + 8 tiles)

@@ -219,6 +219,44 @@ __device__ __forceinline__ void epilogue_pair(const GemmArgs& g, int tm, int tn,
   }
 }
 
+// Whole-tile epilogues stage each wave's outputs in LDS (the ring is free
+// once the K loop is done) and then store rows: 16 contiguous bytes per lane,
+// whole cache lines per 8 or 16 lanes, where the accumulator layout (one row
+// per lane) would touch 32 rows per store instruction.  Each wave stages its
+// own sub-tile in its own ring array, so after one workgroup barrier the
+// waves proceed independently.  A staged row is ROW_CHUNKS 16-byte chunks;
+// chunk c of row r sits at chunk c ^ (r & mask) so the 32 rows one
+// accumulator write touches spread over the LDS banks, while a row read back
+// stays whole.
+template <int ROW_CHUNKS>
+__device__ __forceinline__ int st_off(int r, int c) {
+  constexpr int MASK = ROW_CHUNKS < 16 ? ROW_CHUNKS - 1 : 15;
+  return (r * ROW_CHUNKS + (c ^ (r & MASK))) * 16;
+}
+
+// LDS writes of this wave are complete and visible to its own later reads;
+// the compiler keeps LDS accesses on either side of it in order
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(LGKMCNT0);
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Stores n_rows staged bf16 rows of ROW_CHUNKS * 8 elements to dst (row r at
+// dst + (row0 + r) * ld), rows at or past M skipped.
+template <int ROW_CHUNKS>
+__device__ __forceinline__ void store_staged(const char* st, int n_rows, uint16_t* dst,
+                                             size_t ld, int row0, int M, int lane) {
+  constexpr int RPI = 64 / ROW_CHUNKS;  // rows per store instruction
+  const int c = lane % ROW_CHUNKS;
+  for (int r = lane / ROW_CHUNKS; r < n_rows; r += RPI) {
+    if (row0 + r >= M) break;
+    *reinterpret_cast<uint4*>(dst + (size_t)(row0 + r) * ld + c * 8) =
+        *reinterpret_cast<const uint4*>(st + st_off<ROW_CHUNKS>(r, c));
+  }
+}
+
 // q / k tile epilogue of the 256-row layout: per-head RMSNorm with the
 // learnable scale, then 4-axis RoPE, straight from the fp32 accumulators
 // (the same operations the standalone rope4 kernel applies to stored q, k).
@@ -228,7 +266,7 @@ __device__ __forceinline__ void epilogue_pair(const GemmArgs& g, int tm, int tn,
 // sits in lane ln ^ 32.  Pair p of an axis is dims (2 p, 2 p + 1), turned by
 // pos_axis * theta^(-2 p / 32) radians.
 __device__ __forceinline__ void epilogue_qk(const GemmArgs& g, const f32x16 (&acc)[4][4], int tm,
-                                            int tn, int wm, int wn, int lane) {
+                                            int tn, int wm, int wn, int lane, char* st) {
   constexpr int BM = 256, MB = 4, NB = 4;
   const int ln = lane & 31, hl = lane >> 5;
   const int which = tn * BN / g.D;  // 0: q, 1: k
@@ -270,7 +308,6 @@ __device__ __forceinline__ void epilogue_qk(const GemmArgs& g, const f32x16 (&ac
     const float rstd = rsqrtf(ss * (1.0f / 128.0f) + g.qk_eps);
     if (row >= g.M) continue;
     const int pa[4] = {p4[i].x, p4[i].y, p4[i].z, p4[i].w};
-    uint16_t* const dr = dst + (size_t)row * g.D + c0 + 4 * hl;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const double pj = (double)pa[j];
@@ -292,35 +329,143 @@ __device__ __forceinline__ void epilogue_qk(const GemmArgs& g, const f32x16 (&ac
           y[2 * pr] = x[2 * pr] * cs - x[2 * pr + 1] * sn;
           y[2 * pr + 1] = x[2 * pr] * sn + x[2 * pr + 1] * cs;
         }
-        *reinterpret_cast<uint2*>(dr + j * 32 + 8 * rr) = pack4(y[0], y[1], y[2], y[3]);
+        // staged at row i 32 + ln, columns j 32 + 8 rr + 4 hl .. + 3
+        *reinterpret_cast<uint2*>(st + st_off<16>(i * 32 + ln, 4 * j + rr) + 8 * hl) =
+            pack4(y[0], y[1], y[2], y[3]);
       }
     }
   }
+  wave_lds_sync();
+  store_staged<16>(st, MB * 32, dst + c0, g.D, tm * BM + wm * MB * 32, g.M, lane);
 }
 
-template <int EPI, int BM>
-__device__ __forceinline__ void epilogue(const GemmArgs& g,
-                                         const f32x16 (&acc)[Tile<BM>::MB][Tile<BM>::NB], int tm,
-                                         int tn, int wm, int wn, int lane) {
+// Output projection of a whole tile: y = x + gate * r, staged in passes of
+// PASS_RB 32-row blocks of the wave's fp32 r (24 KB for the 224-row layout's
+// 64 columns, 32 KB for the 256-row layout's 128), with every residual and
+// gate load of a pass issued before its staging writes.  x may be y (in
+// place): each element is read before it is written, by the same lane.
+template <int BM>
+__device__ __forceinline__ void epilogue_out(const GemmArgs& g,
+                                             const f32x16 (&acc)[Tile<BM>::MB][Tile<BM>::NB],
+                                             int tm, int tn, int wm, int wn, int lane, char* st) {
   constexpr int MB = Tile<BM>::MB, NB = Tile<BM>::NB;
-  if constexpr (EPI == EPI_IN && BM == 256) {
-    if (tn < 2 * g.D / BN) {  // q or k
-      epilogue_qk(g, acc, tm, tn, wm, wn, lane);
-      return;
+  constexpr int RC = NB * 32 / 4;         // fp32 16-byte chunks per staged row (16 or 32)
+  constexpr int OC = NB * 32 / 8;         // bf16 16-byte chunks per output row (8 or 16)
+  constexpr int RPI = 64 / OC;            // output rows per wave instruction
+  constexpr int PASS_RB = BM == 224 ? 3 : 2;
+  constexpr int ITERS = PASS_RB * 32 / RPI;
+  const int ln = lane & 31, hl = lane >> 5;
+  const bool use_gate = !(g.flags & 2u), use_res = !(g.flags & 1u);
+  const int c = lane % OC;
+  const int col = tn * BN + wn * NB * 32 + c * 8;  // this lane's 8 output columns
+#pragma unroll
+  for (int p = 0; p * PASS_RB < MB; ++p) {
+    const int rb0 = p * PASS_RB;
+    const int row0 = tm * BM + (wm * MB + rb0) * 32;
+    uint4 xv[ITERS], gv[ITERS];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int row = min(row0 + it * RPI + lane / OC, g.M - 1);
+      xv[it] = use_res ? *reinterpret_cast<const uint4*>(g.x + (size_t)row * g.D + col)
+                       : make_uint4(0u, 0u, 0u, 0u);
+      gv[it] = use_gate ? *reinterpret_cast<const uint4*>(
+                              g.mod + (size_t)stream_of(row, g.e0, g.e1) * 3 * g.D + 2 * g.D + col)
+                        : make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
     }
+#pragma unroll
+    for (int i = rb0; i < rb0 + PASS_RB && i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const f32x16& a = acc[i][j];
+          // row (i - rb0) 32 + ln, columns j 32 + 8 rr + 4 hl .. + 3
+          *reinterpret_cast<float4*>(st + st_off<RC>((i - rb0) * 32 + ln, 8 * j + 2 * rr + hl)) =
+              make_float4(a[4 * rr], a[4 * rr + 1], a[4 * rr + 2], a[4 * rr + 3]);
+        }
+    wave_lds_sync();
+    const int n_rows = (min(MB, rb0 + PASS_RB) - rb0) * 32;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int r = it * RPI + lane / OC;
+      if (r >= n_rows || row0 + r >= g.M) continue;
+      const float4 r0 = *reinterpret_cast<const float4*>(st + st_off<RC>(r, 2 * c));
+      const float4 r1 = *reinterpret_cast<const float4*>(st + st_off<RC>(r, 2 * c + 1));
+      const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+      const uint32_t xw[4] = {xv[it].x, xv[it].y, xv[it].z, xv[it].w};
+      const uint32_t gw[4] = {gv[it].x, gv[it].y, gv[it].z, gv[it].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        o[t] = pack2(fmaf(lo2f(gw[t]), rv[2 * t], lo2f(xw[t])),
+                     fmaf(hi2f(gw[t]), rv[2 * t + 1], hi2f(xw[t])));
+      *reinterpret_cast<uint4*>(g.y + (size_t)(row0 + r) * g.D + col) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    wave_lds_sync();  // the next pass rewrites the staging rows
   }
+  (void)ln;
+  (void)hl;
+}
+
+// Input projection of a whole tile (256-row layout): q / k heads through the
+// norm + RoPE epilogue, v heads and the SwiGLU product m, each staged and
+// stored by rows.
+__device__ __forceinline__ void epilogue_in(const GemmArgs& g, const f32x16 (&acc)[4][4], int tm,
+                                            int tn, int wm, int wn, int lane, char* st) {
+  constexpr int BM = 256, MB = 4, NB = 4;
+  const int ln = lane & 31, hl = lane >> 5;
+  const int n_qkv = 3 * g.D / BN;
+  if (tn < 2 * g.D / BN) {  // q or k
+    epilogue_qk(g, acc, tm, tn, wm, wn, lane, st);
+    return;
+  }
+  const int row0 = tm * BM + wm * MB * 32;
+  if (tn < n_qkv) {  // v: one head per wave
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const f32x16& a = acc[i][j];
+          *reinterpret_cast<uint2*>(st + st_off<16>(i * 32 + ln, 4 * j + rr) + 8 * hl) =
+              pack4(a[4 * rr], a[4 * rr + 1], a[4 * rr + 2], a[4 * rr + 3]);
+        }
+    wave_lds_sync();
+    store_staged<16>(st, MB * 32, g.v + (tn * BN - 2 * g.D + wn * NB * 32), g.D, row0, g.M,
+                     lane);
+    return;
+  }
+  // MLP tile: blocks 2 jp (gate) and 2 jp + 1 (up) of the same 32 hidden
+  // units; the wave's 64 units are staged as 8 chunks per row
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int jp = 0; jp < NB / 2; ++jp)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const f32x16& x0 = acc[i][2 * jp];
-        const f32x16& x1 = acc[i][2 * jp + 1];
-        const float a[4] = {x0[4 * rr], x0[4 * rr + 1], x0[4 * rr + 2], x0[4 * rr + 3]};
-        const float b[4] = {x1[4 * rr], x1[4 * rr + 1], x1[4 * rr + 2], x1[4 * rr + 3]};
-        epilogue_pair<EPI, BM>(g, tm, tn, wm, wn, lane, i, jp, rr, a, b);
+        const f32x16& a = acc[i][2 * jp];
+        const f32x16& b = acc[i][2 * jp + 1];
+        *reinterpret_cast<uint2*>(st + st_off<8>(i * 32 + ln, 4 * jp + rr) + 8 * hl) =
+            pack4(silu(a[4 * rr]) * b[4 * rr], silu(a[4 * rr + 1]) * b[4 * rr + 1],
+                  silu(a[4 * rr + 2]) * b[4 * rr + 2], silu(a[4 * rr + 3]) * b[4 * rr + 3]);
       }
+  wave_lds_sync();
+  const int hid0 = (tn - n_qkv) * 128 + wn * (NB / 2) * 32;
+  store_staged<8>(st, MB * 32, g.cat + g.D + hid0, (size_t)(g.D + g.F), row0, g.M, lane);
+}
+
+template <int EPI, int BM>
+__device__ __forceinline__ void epilogue(const GemmArgs& g,
+                                         const f32x16 (&acc)[Tile<BM>::MB][Tile<BM>::NB], int tm,
+                                         int tn, int wm, int wn, int lane, char* st) {
+  if constexpr (EPI == EPI_IN) {
+    static_assert(BM == 256, "the input projection uses the 256-row layout");
+    epilogue_in(g, acc, tm, tn, wm, wn, lane, st);
+  } else {
+    epilogue_out<BM>(g, acc, tm, tn, wm, wn, lane, st);
+  }
 }
 
 // FP8 mode: multiplies a whole tile's accumulators by the rowwise scales,
@@ -599,7 +744,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 
     if constexpr (!SPLIT) {
       if constexpr (F8) scale_acc<EPI, BM>(g, acc, tm, tn, wm, wn, lane);
-      epilogue<EPI, BM>(g, acc, tm, tn, wm, wn, lane);
+      // every wave is past its last fragment read of the ring before any
+      // wave stages into it; wave w stages into ring array w (>= 28 KB)
+      __syncthreads();
+      char* const st = reinterpret_cast<char*>(wave == 0   ? s_a0
+                                               : wave == 1 ? s_a1
+                                               : wave == 2 ? s_w0
+                                                           : s_w1);
+      epilogue<EPI, BM>(g, acc, tm, tn, wm, wn, lane, st);
     } else {
       float4* dst = partial_slot<BM>(g, slot, wave, lane);
 #pragma unroll

@@ -460,3 +460,39 @@ def test_fp8_host_errors(lib):
     assert lib.dit_quantize_rows_fp8(4, 16, c(P), c(BAD), c(P + (2 << 30)), None) == ALIGN
     assert lib.dit_quantize_rows_fp8(4, 16, c(P), c(P + 64), c(P + (2 << 30)), None) == ARG
     assert lib.dit_quantize_rows_fp8(0, 16, None, None, None, None) == OK
+
+
+def test_struct_layouts_match_a_c_compiler(tmp_path):
+    # sizes and field offsets of every struct in include/dit.h, as gcc lays
+    # them out, against the ctypes mirrors the binding passes by pointer
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    rocm_inc = "/opt/rocm/include"
+    if gcc is None or not os.path.exists(os.path.join(rocm_inc, "hip", "hip_runtime_api.h")):
+        pytest.skip("gcc or the HIP headers are not available")
+    structs = {"dit_block_desc": ops.BlockDesc, "dit_stack_desc": ops.StackDesc,
+               "dit_block_params": ops.BlockParams, "dit_model_desc": ops.ModelDesc,
+               "dit_block_weights": ops.BlockWeights, "dit_model_weights": ops.ModelWeights}
+    lines = ["#define __HIP_PLATFORM_AMD__ 1", "#include <stdio.h>", "#include <stddef.h>",
+             '#include "dit.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    r = subprocess.run([gcc, "-std=c11", "-I", os.path.dirname(HEADER), "-I", rocm_inc,
+                        str(src), "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                               check=True).stdout.splitlines():
+        name, field, val = line.split()
+        got[(name, field)] = int(val)
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for fname, _ in cls._fields_:
+            assert got[(cname, fname)] == getattr(cls, fname).offset, (cname, fname)

@@ -136,6 +136,19 @@ def test_fp8_block_narrow_width():
     check_fp8(cfg, inputs.make_block_inputs(cfg, seed=4), rows=rows, vs_bf16=False)
 
 
+def test_fp8_block_qk_scales():
+    # non-unit QK-norm scales through the FP8 input projection's epilogue
+    require_gpu()
+    cfg = configs.C1
+    d = inputs.make_block_inputs(cfg, seed=5)
+    g = oracle.widen_bf16(inputs.normal_bf16((2, cfg.head_dim), 0.2, 5, 77, 1))
+    d["q_scale"] = inputs.f64_to_bf16_bits(3.0 * (1.0 + g[0]))
+    d["k_scale"] = inputs.f64_to_bf16_bits(1.0 + g[1])
+    _WQ.pop((cfg.name, cfg.config_id), None)
+    log("fp8 block c1 with qk scales")
+    check_fp8(cfg, d, vs_bf16=False)
+
+
 def test_fp8_zero_gate_returns_x():
     require_gpu()
     cfg = configs.C1

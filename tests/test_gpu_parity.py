@@ -133,9 +133,21 @@ def test_attn_softmax_scale_argument():
 
 # ---------------------------------------------------------- dit_block_fwd ----
 
-def check_block(cfg, seed=0, rows=None):
+def qk_scales(d, seed, gq=3.0):
+    """Per-dim QK-norm scales: q around gq (peaked logits), k around 1."""
+    dh = d["q_scale"].shape[0]
+    g = oracle.widen_bf16(inputs.normal_bf16((2, dh), 0.2, seed, 77, 1))
+    d["q_scale"] = inputs.f64_to_bf16_bits(gq * (1.0 + g[0]))
+    d["k_scale"] = inputs.f64_to_bf16_bits(1.0 + g[1])
+    return d
+
+
+def check_block(cfg, seed=0, rows=None, scaled=False):
     d = inputs.make_block_inputs(cfg, seed=seed)
-    log(f"block {cfg.name} N={cfg.N} rows={'all' if rows is None else len(rows)}")
+    if scaled:
+        d = qk_scales(d, seed)
+    log(f"block {cfg.name} N={cfg.N} rows={'all' if rows is None else len(rows)}"
+        f"{' qk scales' if scaled else ''}")
     dv = to_dev(d)
     y = widen(run_block(dv, cfg))
     r = widen(run_block(dv, cfg, flags=ops.DIT_F_NO_RESIDUAL | ops.DIT_F_NO_GATE))
@@ -150,6 +162,13 @@ def check_block(cfg, seed=0, rows=None):
 
 def test_block_parity_c1_full():
     check_block(configs.C1)
+
+
+def test_block_parity_qk_scales():
+    # learnable QK-norm scales away from one (q around 3: peaked logits) go
+    # through the fused norm + RoPE epilogue of the input projection
+    check_block(configs.C1, seed=4, scaled=True)
+    check_block(configs.C2, seed=4, rows=sample_rows(configs.C2, n_random=24), scaled=True)
 
 
 def test_block_parity_ragged_three_streams():

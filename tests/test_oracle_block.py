@@ -192,3 +192,31 @@ def test_bf16_bits_are_widened_exactly():
 def test_rel_l2():
     assert oracle.rel_l2([3.0, 4.0], [3.0, 4.0]) == 0.0
     assert oracle.rel_l2([3.0, 4.0 + 5.0], [3.0, 4.0]) == pytest.approx(1.0)
+
+
+def test_fused_projections_equal_the_separate_layers():
+    # the input projection is to_q, to_k, to_v and ff.linear_in stacked by
+    # rows, and the output projection is to_out.0 plus ff.linear_out: the
+    # block equals the composition of the separate products
+    rng = np.random.default_rng(21)
+    n, D, F = [9, 4], 16, 24
+    N = sum(n)
+    x = rng.standard_normal((N, D))
+    mod = rng.standard_normal((2, 3, D)) * 0.3
+    pos = np.zeros((N, 4), dtype=np.int64)
+    pos[:9, 1], pos[:9, 2], pos[9:, 0] = np.arange(9) // 3, np.arange(9) % 3, np.arange(4)
+    w_q, w_k, w_v = (rng.standard_normal((D, D)) / 4 for _ in range(3))
+    w_lin = rng.standard_normal((2 * F, D)) / 4
+    w_o, w_lo = rng.standard_normal((D, D)) / 4, rng.standard_normal((D, F)) / 5
+    g = np.ones(8)
+    out = oracle.block_ref(x, mod, pos, np.concatenate([w_q, w_k, w_v, w_lin]),
+                           np.concatenate([w_o, w_lo], axis=1), g, g, n, 2, 8, F)
+    u = oracle.adaln_ref(x, mod, n, 1e-6)
+    q = oracle.rope4_ref(oracle.head_rms_norm((u @ w_q.T).reshape(N, 2, 8), g, 1e-6), pos, 1e4)
+    k = oracle.rope4_ref(oracle.head_rms_norm((u @ w_k.T).reshape(N, 2, 8), g, 1e-6), pos, 1e4)
+    v = (u @ w_v.T).reshape(N, 2, 8)
+    o = oracle.attention_ref(q, k, v, 1 / np.sqrt(8)).reshape(N, D)
+    lin = u @ w_lin.T
+    m = oracle.swiglu_ref(lin[:, :F], lin[:, F:])
+    r = o @ w_o.T + m @ w_lo.T
+    assert np.allclose(out["r"], r, rtol=1e-12, atol=1e-12)

@@ -15,7 +15,8 @@ at the same shapes (`--no-stack` skips both), and
 another one block of the long 2048^2 editing sequence (2048^2 image, one
 2048^2 reference, 160 text tokens; `--no-long` skips it).  `block_fp8` times
 the same block with FP8 (rowwise e4m3) projections (`--no-fp8` skips it); it
-is a secondary line, not the bf16 metric.
+is a secondary line, not the bf16 metric.  `stage1_c3` times the two stage-1
+blocks of c3 (4,096 image tokens; 80 text tokens, weight-streaming bound).
 
 Prints one JSON line.
 """
@@ -293,6 +294,56 @@ def block_fp8(torch, configs, ops, timing, cfg, x, mod, pos, qs, ks, weights, st
     }
 
 
+def stage1_c3(torch, configs, ops, steps: int, warmup: int) -> dict:
+    """The two stage-1 blocks of c3 as independent dit_block_fwd calls: the
+    4,096-token image block (MFMA-bound) and the 80-token text block, whose
+    time is set by streaming its 245 MB of weights (4 rotating weight sets,
+    so they come from HBM)."""
+    D, F, d = configs.WIDTH, configs.MLP_HIDDEN, configs.HEAD_DIM
+    gen = torch.Generator(device="cuda").manual_seed(31)
+
+    def rnd(shape, std):
+        return (torch.randn(shape, generator=gen, device="cuda") * std).to(torch.bfloat16)
+
+    ones = torch.ones(d, dtype=torch.bfloat16, device="cuda")
+    weights = [(rnd((3 * D + 2 * F, D), D ** -0.5), rnd((D, D + F), (D + F) ** -0.5))
+               for _ in range(4)]
+    from flow_matching_diffusion_adaln_amd import inputs
+    out = {}
+    for cfg in (configs.C3_IMG, configs.C3_TXT):
+        x = rnd((cfg.N, D), 1.0)
+        mod = rnd((1, 3, D), 0.1 ** 0.5)
+        pos = torch.from_numpy(inputs.positions(cfg)).cuda()
+        desc = ops.make_desc(cfg.n_tokens)
+        ws = ops.alloc_workspace(desc)
+        y = torch.empty_like(x)
+        n = steps * 4
+
+        def step(i):
+            w_in, w_out = weights[i % 4]
+            ops.block_fwd(x, mod, pos, w_in, w_out, ones, ones, desc, y=y, workspace=ws)
+
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            step(i)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / n
+        assert bool(torch.isfinite(y.float()).all())
+        wbytes = 2.0 * ((3 * D + 2 * F) * D + D * (D + F))
+        out[cfg.name] = {"N": cfg.N, "ms_per_block": round(ms, 4),
+                         "tflops": round(cfg.flop() / (ms * 1e-3) / 1e12, 2),
+                         "weight_gbs": round(wbytes / (ms * 1e-3) / 1e9, 1),
+                         "weight_frac_hbm_peak": round(wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    out["workload"] = ("c3: stage-1 image block (4096 tokens, t=0.9) and stage-1 text block "
+                       "(80 tokens, t=0), independent calls, 4 rotating weight sets")
+    out["sum_ms"] = round(out["c3_img"]["ms_per_block"] + out["c3_txt"]["ms_per_block"], 4)
+    out["steps"], out["warmup"] = steps * 4, warmup
+    return out
+
+
 def block_long(torch, configs, ops, timing, steps: int, warmup: int) -> dict:
     """One block forward of the long editing sequence (N = 32,928) with
     device-generated random weights, timed per stage with HIP events."""
@@ -496,6 +547,8 @@ def main():
                                         weights, args.steps, args.warmup)
     if not args.no_stack:
         result["sampler_c5"] = sampler_c5(torch, configs, ops, steps=3, warmup=1)
+    if not args.no_stack:
+        result["stage1_c3"] = stage1_c3(torch, configs, ops, steps=5, warmup=4)
     if not args.no_long:
         result["block_edit2048"] = block_long(torch, configs, ops, timing, steps=5, warmup=1)
 

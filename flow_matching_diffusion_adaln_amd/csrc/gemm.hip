@@ -70,6 +70,7 @@ struct GemmArgs {
   const uint16_t* q_scale;  // [128] bf16
   const uint16_t* k_scale;  // [128] bf16
   float qk_eps;
+  float theta;
   double rope_rev[16];     // theta^(-2j / 32) / (2 pi): turns per position step of pair j
   // output projection
   const uint16_t* x;  // residual [M, D]
@@ -755,7 +756,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     } else {
       float4* dst = partial_slot<BM>(g, slot, wave, lane);
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
+      for (int i = 0; i < MB; ++i) {
+        // 32-row blocks wholly past M are neither stored nor read back
+        if (tm * BM + (wm * MB + i) * 32 >= g.M) continue;
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -764,6 +767,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
             dst[((i * NB + j) * 4 + rr) * 64] =
                 make_float4(a[4 * rr], a[4 * rr + 1], a[4 * rr + 2], a[4 * rr + 3]);
           }
+      }
     }
   };
 
@@ -804,6 +808,8 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
   const int wm = wave / T::WN, wn = wave % T::WN;
   int tm, tn;
   tile_coords<BM>(g, g.n_dp + t_rel, tm, tn);
+  // the split items store no 32-row block that lies wholly past M
+  if (tm * BM + (wm * MB + i) * 32 >= g.M) return;
   const int upt = g.KT / g.unit;
   const int units = g.n_tail * upt;
   const int ua = t_rel * upt, ub = ua + upt;  // this tile's units
@@ -877,7 +883,12 @@ Plan make_plan(int bm, int M, int KT, int num_n, bool can_split) {
   // a 224-row tile takes about as long as a 256-row one (the k loop's fixed
   // per-step latency dominates), so cost is counted in tiles
   const float tile_time = 1.0f;
-  if (can_split && full >= 1 && tail > 0 && 2 * tail <= cus) {
+  // a last round at most half full is split; so is a launch with at most
+  // half as many tiles as CUs (a short sequence, e.g. an 80- or 160-token
+  // text stage): then every tile is cut, so all CUs share the weight stream
+  const bool split_tail = full >= 1 && tail > 0 && 2 * tail <= cus;
+  const bool split_all = full == 0 && tail > 0 && 2 * tail <= cus;
+  if (can_split && (split_tail || split_all)) {
     p.n_dp = full * cus;
     p.n_tail = tail;
     p.n_pieces = min(min(cus, kMaxPieces), tail * upt);
@@ -907,6 +918,7 @@ Plan pick_plan(int M, int KT, int num_n, bool can_split) {
 template <int EPI, bool F8>
 hipError_t launch(GemmArgs g, hipStream_t stream) {
   const bool can_split = g.partial != nullptr;
+  bool qk_after = false;
   g.KT = g.K * (F8 ? 1 : 2) / 128;
   Plan p;
   if constexpr (EPI == EPI_IN) {
@@ -916,8 +928,11 @@ hipError_t launch(GemmArgs g, hipStream_t stream) {
     // the last in tile order, i.e. the highest N tiles: MLP ones).
     p = make_plan(256, g.M, g.KT, g.num_n, can_split);
     const int num_m = (g.M + 255) / 256;
-    if (p.n_tail && (p.n_dp / (GROUP_N * num_m)) * GROUP_N < 2 * g.D / BN)
+    if (p.n_tail && p.n_dp > 0 && (p.n_dp / (GROUP_N * num_m)) * GROUP_N < 2 * g.D / BN)
       p = make_plan(256, g.M, g.KT, g.num_n, false);
+    // with every tile split, the fix-up stores q and k as summed, and the
+    // norm + RoPE pass runs on them afterwards
+    qk_after = p.n_tail > 0 && p.n_dp == 0;
   } else {
     p = pick_plan(g.M, g.KT, g.num_n, can_split);
   }
@@ -935,6 +950,12 @@ hipError_t launch(GemmArgs g, hipStream_t stream) {
     if (g.n_tail)
       hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 256, F8>), dim3(g.n_tail * 256 * BN / 8 / 256),
                          dim3(256), 0, stream, g);
+    if (qk_after) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_rope4(g.q, g.k, g.pos, g.q_scale, g.k_scale, g.M, g.D / 128, g.theta,
+                          g.qk_eps, stream);
+    }
   } else if constexpr (EPI == EPI_OUT) {
     if (g.unit == 6)
       hipLaunchKernelGGL((gemm_kernel<EPI, 224, 3, F8>), dim3(grid), dim3(256), 0, stream, g);
@@ -959,6 +980,7 @@ GemmArgs in_args(const void* u, const void* w_in, int M, int D, int F, uint16_t*
   g.q_scale = q_scale;
   g.k_scale = k_scale;
   g.qk_eps = qk_eps;
+  g.theta = theta;
   const double two_pi = 6.283185307179586;
   for (int j = 0; j < 16; ++j) g.rope_rev[j] = pow((double)theta, -2.0 * j / 32.0) / two_pi;
   g.partial = partial;

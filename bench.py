@@ -12,8 +12,9 @@ is timed once on the host as a baseline and its output gives the parity of
 the timed configuration.  A secondary field times one guided denoise step of
 the two-stage stack (c5) through dit_stack_fwd and the flow-matching sampler
 at the same shapes (`--no-stack` skips both), and
-another one block of the long 2048^2 editing sequence (2048^2 image, one
-2048^2 reference, 160 text tokens; `--no-long` skips it).  `block_fp8` times
+blocks of the 1024^2 edit with one reference (c4, 8,352 tokens) and of the
+long 2048^2 edit (2048^2 image, one 2048^2 reference, 160 text tokens;
+`--no-long` skips both).  `block_fp8` times
 the same block with FP8 (rowwise e4m3) projections (`--no-fp8` skips it); it
 is a secondary line, not the bf16 metric.  `stage1_c3` times the two stage-1
 blocks of c3 (4,096 image tokens; 80 text tokens, weight-streaming bound).
@@ -344,10 +345,10 @@ def stage1_c3(torch, configs, ops, steps: int, warmup: int) -> dict:
     return out
 
 
-def block_long(torch, configs, ops, timing, steps: int, warmup: int) -> dict:
-    """One block forward of the long editing sequence (N = 32,928) with
-    device-generated random weights, timed per stage with HIP events."""
-    cfg = configs.EDIT_2048
+def block_secondary(torch, configs, ops, timing, cfg, steps: int, warmup: int) -> dict:
+    """One block forward of another sequence (the 1024^2 edit with one
+    reference, c4, or the long 2048^2 edit) with device-generated random
+    weights, timed per stage with HIP events."""
     D, F, d = cfg.width, cfg.mlp_hidden, cfg.head_dim
     from flow_matching_diffusion_adaln_amd import inputs
     gen = torch.Generator(device="cuda").manual_seed(777)
@@ -550,7 +551,10 @@ def main():
     if not args.no_stack:
         result["stage1_c3"] = stage1_c3(torch, configs, ops, steps=5, warmup=4)
     if not args.no_long:
-        result["block_edit2048"] = block_long(torch, configs, ops, timing, steps=5, warmup=1)
+        result["block_c4"] = block_secondary(torch, configs, ops, timing, configs.C4, steps=10,
+                                             warmup=2)
+        result["block_edit2048"] = block_secondary(torch, configs, ops, timing,
+                                                   configs.EDIT_2048, steps=5, warmup=1)
 
     if not args.no_cpu_baseline:
         ref, sec, threads, blas, n_blocks = cpu_baseline(d, cfg)

@@ -1,6 +1,7 @@
-// C ABI of the DiT block library: host-side validation, workspace layout and
-// the launch sequence of dit_block_fwd.  Every check runs before the first
-// launch, so an error leaves all outputs untouched.
+// C ABI of the DiT block library: host-side validation, workspace layouts and
+// the launch sequences of the block (bf16 and FP8), the two-stage stack with
+// classifier-free guidance and the flow-matching sampler.  Every check runs
+// before the first launch, so an error leaves all outputs untouched.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>

@@ -1,4 +1,4 @@
-// Internal launchers of the block's kernels (host side).  Arguments are
+// Internal launchers of the library's kernels (host side).  Arguments are
 // validated by the C ABI layer before any of these is called.
 #pragma once
 

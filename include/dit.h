@@ -16,12 +16,18 @@
  * carry the modulation of the current timestep t, text and reference tokens
  * the modulation of t = 0; the modulation vectors themselves are inputs.
  *
+ * Around the block, in sections of their own below: the block with FP8
+ * projections, the two-stage stack with classifier-free guidance, and the
+ * flow-matching sampler (timestep modulation, embedders, output layers and
+ * the guided Euler step).
+ *
  * Conventions shared by every call:
  *   - Tensors are device pointers owned by the caller, row-major, bf16 stored
  *     as 16-bit patterns unless stated.  They must be 16-byte aligned.
  *   - Work is enqueued on `stream` (0 = the null stream); calls return once
- *     enqueued.  The library never allocates, frees or synchronizes, and keeps
- *     no mutable global state, so calls may come from several threads.
+ *     enqueued.  The library never allocates, frees or synchronizes; its only
+ *     global state is a per-device cache of the CU count, so calls may come
+ *     from several threads.
  *   - Validation runs on the host before any launch; on error nothing is
  *     launched and outputs are untouched.  Errors are negative status codes,
  *     and dit_status_str() names them.
@@ -31,8 +37,8 @@
  *     n_heads * 128 with n_heads a multiple of 4 and width at most 8192,
  *     mlp_hidden a multiple of 128 (at most 65536), at most DIT_MAX_TOKENS
  *     tokens, and every tensor (including the [N, D + F] internal buffer)
- *     under 4 GiB; larger calls return DIT_ERR_UNSUPPORTED.  The FLUX.3 Image Klein block is width 3072,
- *     24 heads, mlp_hidden 9216.
+ *     under 4 GiB; larger calls return DIT_ERR_UNSUPPORTED.  The FLUX.3
+ *     Image Klein block is width 3072, 24 heads, mlp_hidden 9216.
  *   - A token count of 0 is a valid empty call: DIT_OK, nothing launched.
  */
 #ifndef DIT_H

@@ -40,6 +40,7 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace dit {
@@ -845,16 +846,17 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
 
 // Compute units of the current device (queried once per device).
 int device_cus() {
-  static int cached[64] = {0};
+  // several host threads may fill an entry at once; they store the same value
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Work plan of one GEMM launch.  With one workgroup per CU at a time, tiles

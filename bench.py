@@ -9,7 +9,9 @@ between steps so the 245 MB of one block's weights is not served from the
 steps gives per-stage times from HIP events the library records on the work
 stream between its kernels.  The fp64 CPU oracle of the same block
 is timed once on the host as a baseline and its output gives the parity of
-the timed configuration.  A secondary field times one guided denoise step of
+the timed configuration (y, and the branch r read with the residual and gate
+switched off); dit_attn_fwd alone is checked at sampled query rows against
+the oracle's attention on the same seeded bf16 q, k, v.  A secondary field times one guided denoise step of
 the two-stage stack (c5) through dit_stack_fwd and the flow-matching sampler
 at the same shapes (`--no-stack` skips both), and
 blocks of the 1024^2 edit with one reference (c4, 8,352 tokens) and of the
@@ -345,6 +347,23 @@ def stage1_c3(torch, configs, ops, steps: int, warmup: int) -> dict:
     return out
 
 
+def attn_parity(torch, oracle, inputs, ops, N: int, n_rows: int = 64) -> dict:
+    """dit_attn_fwd alone at N tokens on seeded bf16 q, k, v (24 x 128 heads),
+    against the oracle's attention on the same bf16 values, at sampled query
+    rows (the oracle computes each row against all N keys)."""
+    d = inputs.make_attn_inputs(N, 24, 128, seed=6, logit_std=1.0)
+    q, k, v = (ops.to_device_bf16(d[n]) for n in ("q", "k", "v"))
+    o = ops.attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, N - 1],
+                                     np.random.default_rng(1).choice(N, n_rows, replace=False)]))
+    qh, kh, vh = (oracle.widen_bf16(d[n]) for n in ("q", "k", "v"))
+    ref = oracle.attention_ref(qh[rows], kh, vh, 128 ** -0.5)
+    got = oracle.widen_bf16(ops.to_host_bits(o))[rows]
+    return {"relL2_attn": oracle.rel_l2(got, ref), "attn_bound": 5e-3,
+            "attn_rows_checked": int(len(rows))}
+
+
 def block_secondary(torch, configs, ops, timing, cfg, steps: int, warmup: int) -> dict:
     """One block forward of another sequence (the 1024^2 edit with one
     reference, c4, or the long 2048^2 edit) with device-generated random
@@ -490,10 +509,18 @@ def main():
     tflops = flop / (ms_per_step * 1e-3) / 1e12
     gemm_in_tflops = gemm_in_flop / (st["gemm_in"] * 1e-3) / 1e12
 
-    # parity of this exact configuration (weight set 0) against the oracle
+    # parity of this exact configuration (weight set 0) against the oracle:
+    # y, and the branch r (read with the residual and gate switched off)
     step(0)
     torch.cuda.synchronize()
     y_set0 = oracle.widen_bf16(ops.to_host_bits(y))
+    r = torch.empty_like(x)
+    ops.block_fwd(x, mod, pos, weights[0][0], weights[0][1], qs, ks,
+                  ops.make_desc(cfg.n_tokens, flags=ops.DIT_F_NO_RESIDUAL | ops.DIT_F_NO_GATE),
+                  y=r, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    r_set0 = oracle.widen_bf16(ops.to_host_bits(r))
+    del r
 
     result = {
         "metric": "DiT joint-block fwd TFLOP/s & ms/block, 4096 img + 160 txt tokens, bf16",
@@ -515,6 +542,7 @@ def main():
         },
         "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "block_ms_events_median": round(float(np.median(block_ms_ev)), 4),
+        "block_ms_events_min": round(float(np.min(block_ms_ev)), 4),
         "stage_ms_mean": {k: round(v, 4) for k, v in st.items()},
         "stage_ms_median": {k: round(v, 4) for k, v in st_med.items()},
         "attn": {
@@ -567,10 +595,13 @@ def main():
                       f"float64, run {n_blocks} times ({n_blocks * sec:.1f} s wall, "
                       f"{sec:.2f} s per block), BLAS {blas}, host {cpu_model()}",
             "seconds_per_block": round(sec, 3),
+            "cpu_model": cpu_model(),
         }
         result["parity"] = {
             "relL2_y": oracle.rel_l2(y_set0, ref["y"]),
+            "relL2_r": oracle.rel_l2(r_set0, ref["r"]),
             "bound": 1e-2,
+            **attn_parity(torch, oracle, inputs, ops, cfg.N),
         }
     print(json.dumps(result), flush=True)
     return 0

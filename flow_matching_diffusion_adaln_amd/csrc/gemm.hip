@@ -882,8 +882,9 @@ Plan make_plan(int bm, int M, int KT, int num_n, bool can_split) {
   p.tiles = ((M + bm - 1) / bm) * num_n;
   const int full = p.tiles / cus, tail = p.tiles - full * cus;
   const int upt = KT / unroll_period(KT);
-  // a 224-row tile takes about as long as a 256-row one (the k loop's fixed
-  // per-step latency dominates), so cost is counted in tiles
+  // cost is counted in rounds of whole tiles; a 224-row tile has 7/8 of a
+  // 256-row tile's MFMAs, so when both layouts need as many rounds the
+  // shorter tile wins the tie (pick_plan)
   const float tile_time = 1.0f;
   // a last round at most half full is split; so is a launch with at most
   // half as many tiles as CUs (a short sequence, e.g. an 80- or 160-token

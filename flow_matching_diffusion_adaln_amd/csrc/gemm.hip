@@ -341,6 +341,89 @@ __device__ __forceinline__ void epilogue_qk(const GemmArgs& g, const f32x16 (&ac
   store_staged<16>(st, MB * 32, dst + c0, g.D, tm * BM + wm * MB * 32, g.M, lane);
 }
 
+// q / k tile epilogue of the 224-row layout (1 x 4 waves of 224 x 64): a
+// head's 128 dims are split over waves wn and wn ^ 1, 64 each, so the two
+// halves of each row's sum of squares meet in LDS (s_rs, 224 floats per
+// wave).  Wave wn holds axes 2 (wn & 1) and 2 (wn & 1) + 1 in its blocks 0
+// and 1; the rest is the 256-row epilogue's norm and rotation.
+__device__ __forceinline__ void epilogue_qk224(const GemmArgs& g, const f32x16 (&acc)[7][2],
+                                               int tm, int tn, int wn, int lane, char* st,
+                                               float* s_rs) {
+  constexpr int BM = 224, MB = 7, NB = 2;
+  const int ln = lane & 31, hl = lane >> 5;
+  const int which = tn * BN / g.D;  // 0: q, 1: k
+  uint16_t* const dst = which ? g.k : g.q;
+  const uint16_t* const scale = which ? g.k_scale : g.q_scale;
+  const int hh = wn & 1;                                  // half of the head
+  const int c0 = tn * BN - which * g.D + wn * NB * 32;    // first dim of this wave
+  uint2 gsc[NB][4];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      gsc[j][rr] = *reinterpret_cast<const uint2*>(scale + (2 * hh + j) * 32 + 8 * rr + 4 * hl);
+  double fr[4][2];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const double f0 = g.rope_rev[4 * rr + pr], f1 = g.rope_rev[4 * rr + 2 + pr];
+      fr[rr][pr] = hl ? f1 : f0;
+    }
+  int4 p4[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int row = tm * BM + i * 32 + ln;
+    p4[i] = reinterpret_cast<const int4*>(g.pos)[min(row, g.M - 1)];
+  }
+  float ss[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a = fmaf(acc[i][j][r], acc[i][j][r], a);
+    ss[i] = a + __shfl_xor(a, 32, 64);
+    if (hl == 0) s_rs[wn * BM + i * 32 + ln] = ss[i];
+  }
+  __syncthreads();  // every wave of the tile is a q or k wave
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int row = tm * BM + i * 32 + ln;
+    const float tot = ss[i] + s_rs[(wn ^ 1) * BM + i * 32 + ln];
+    const float rstd = rsqrtf(tot * (1.0f / 128.0f) + g.qk_eps);
+    if (row >= g.M) continue;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int pax = hh ? (j ? p4[i].w : p4[i].z) : (j ? p4[i].y : p4[i].x);
+      const double pj = (double)pax;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const uint2 gs = gsc[j][rr];
+        const float x[4] = {acc[i][j][4 * rr] * rstd * lo2f(gs.x),
+                            acc[i][j][4 * rr + 1] * rstd * hi2f(gs.x),
+                            acc[i][j][4 * rr + 2] * rstd * lo2f(gs.y),
+                            acc[i][j][4 * rr + 3] * rstd * hi2f(gs.y)};
+        float y[4];
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const double t = pj * fr[rr][pr];
+          const float r = (float)(t - floor(t));
+          const float sn = __builtin_amdgcn_sinf(r), cs = __builtin_amdgcn_cosf(r);
+          y[2 * pr] = x[2 * pr] * cs - x[2 * pr + 1] * sn;
+          y[2 * pr + 1] = x[2 * pr] * sn + x[2 * pr + 1] * cs;
+        }
+        // staged at row i 32 + ln, columns j 32 + 8 rr + 4 hl .. + 3
+        *reinterpret_cast<uint2*>(st + st_off<8>(i * 32 + ln, 4 * j + rr) + 8 * hl) =
+            pack4(y[0], y[1], y[2], y[3]);
+      }
+    }
+  }
+  wave_lds_sync();
+  store_staged<8>(st, MB * 32, dst + c0, g.D, tm * BM, g.M, lane);
+}
+
 // Output projection of a whole tile: y = x + gate * r, staged in passes of
 // PASS_RB 32-row blocks of the wave's fp32 r (24 KB for the 224-row layout's
 // 64 columns, 32 KB for the 256-row layout's 128), with every residual and
@@ -410,20 +493,27 @@ __device__ __forceinline__ void epilogue_out(const GemmArgs& g,
   (void)hl;
 }
 
-// Input projection of a whole tile (256-row layout): q / k heads through the
-// norm + RoPE epilogue, v heads and the SwiGLU product m, each staged and
-// stored by rows.
-__device__ __forceinline__ void epilogue_in(const GemmArgs& g, const f32x16 (&acc)[4][4], int tm,
-                                            int tn, int wm, int wn, int lane, char* st) {
-  constexpr int BM = 256, MB = 4, NB = 4;
+// Input projection of a whole tile: q / k heads through the norm + RoPE
+// epilogue, v heads and the SwiGLU product m, each staged and stored by rows.
+// A wave holds NB * 32 columns: 128 (256-row layout) or 64 (224-row layout).
+template <int BM>
+__device__ __forceinline__ void epilogue_in(const GemmArgs& g,
+                                            const f32x16 (&acc)[Tile<BM>::MB][Tile<BM>::NB],
+                                            int tm, int tn, int wm, int wn, int lane, char* st,
+                                            float* s_rs) {
+  constexpr int MB = Tile<BM>::MB, NB = Tile<BM>::NB;
   const int ln = lane & 31, hl = lane >> 5;
   const int n_qkv = 3 * g.D / BN;
   if (tn < 2 * g.D / BN) {  // q or k
-    epilogue_qk(g, acc, tm, tn, wm, wn, lane, st);
+    if constexpr (BM == 256)
+      epilogue_qk(g, acc, tm, tn, wm, wn, lane, st);
+    else
+      epilogue_qk224(g, acc, tm, tn, wn, lane, st, s_rs);
     return;
   }
   const int row0 = tm * BM + wm * MB * 32;
-  if (tn < n_qkv) {  // v: one head per wave
+  if (tn < n_qkv) {  // v
+    constexpr int RC = NB * 4;  // 16-byte chunks per staged row
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -431,16 +521,18 @@ __device__ __forceinline__ void epilogue_in(const GemmArgs& g, const f32x16 (&ac
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const f32x16& a = acc[i][j];
-          *reinterpret_cast<uint2*>(st + st_off<16>(i * 32 + ln, 4 * j + rr) + 8 * hl) =
+          *reinterpret_cast<uint2*>(st + st_off<RC>(i * 32 + ln, 4 * j + rr) + 8 * hl) =
               pack4(a[4 * rr], a[4 * rr + 1], a[4 * rr + 2], a[4 * rr + 3]);
         }
     wave_lds_sync();
-    store_staged<16>(st, MB * 32, g.v + (tn * BN - 2 * g.D + wn * NB * 32), g.D, row0, g.M,
+    store_staged<RC>(st, MB * 32, g.v + (tn * BN - 2 * g.D + wn * NB * 32), g.D, row0, g.M,
                      lane);
     return;
   }
   // MLP tile: blocks 2 jp (gate) and 2 jp + 1 (up) of the same 32 hidden
-  // units; the wave's 64 units are staged as 8 chunks per row
+  // units; the wave's NB / 2 groups of 32 units are staged as 2 NB chunks
+  // per row
+  constexpr int MC = NB * 2;
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -449,23 +541,23 @@ __device__ __forceinline__ void epilogue_in(const GemmArgs& g, const f32x16 (&ac
       for (int rr = 0; rr < 4; ++rr) {
         const f32x16& a = acc[i][2 * jp];
         const f32x16& b = acc[i][2 * jp + 1];
-        *reinterpret_cast<uint2*>(st + st_off<8>(i * 32 + ln, 4 * jp + rr) + 8 * hl) =
+        *reinterpret_cast<uint2*>(st + st_off<MC>(i * 32 + ln, 4 * jp + rr) + 8 * hl) =
             pack4(silu(a[4 * rr]) * b[4 * rr], silu(a[4 * rr + 1]) * b[4 * rr + 1],
                   silu(a[4 * rr + 2]) * b[4 * rr + 2], silu(a[4 * rr + 3]) * b[4 * rr + 3]);
       }
   wave_lds_sync();
   const int hid0 = (tn - n_qkv) * 128 + wn * (NB / 2) * 32;
-  store_staged<8>(st, MB * 32, g.cat + g.D + hid0, (size_t)(g.D + g.F), row0, g.M, lane);
+  store_staged<MC>(st, MB * 32, g.cat + g.D + hid0, (size_t)(g.D + g.F), row0, g.M, lane);
 }
 
 template <int EPI, int BM>
 __device__ __forceinline__ void epilogue(const GemmArgs& g,
                                          const f32x16 (&acc)[Tile<BM>::MB][Tile<BM>::NB], int tm,
-                                         int tn, int wm, int wn, int lane, char* st) {
+                                         int tn, int wm, int wn, int lane, char* st, float* s_rs) {
   if constexpr (EPI == EPI_IN) {
-    static_assert(BM == 256, "the input projection uses the 256-row layout");
-    epilogue_in(g, acc, tm, tn, wm, wn, lane, st);
+    epilogue_in<BM>(g, acc, tm, tn, wm, wn, lane, st, s_rs);
   } else {
+    (void)s_rs;
     epilogue_out<BM>(g, acc, tm, tn, wm, wn, lane, st);
   }
 }
@@ -536,6 +628,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t s_a2[NA == 3 ? BM * BK : 8];
   __shared__ __attribute__((aligned(16))) uint16_t s_w0[BN * BK];
   __shared__ __attribute__((aligned(16))) uint16_t s_w1[BN * BK];
+  // row sums of squares exchanged by the 224-row q / k epilogue
+  __shared__ float s_rs[EPI == EPI_IN && BM == 224 ? 4 * 224 : 1];
   uint16_t* const ring_a[3] = {s_a0, s_a1, s_a2};
   uint16_t* const ring_w[NW] = {s_w0, s_w1};
 
@@ -753,7 +847,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
                                                : wave == 1 ? s_a1
                                                : wave == 2 ? s_w0
                                                            : s_w1);
-      epilogue<EPI, BM>(g, acc, tm, tn, wm, wn, lane, st);
+      epilogue<EPI, BM>(g, acc, tm, tn, wm, wn, lane, st, s_rs);
     } else {
       float4* dst = partial_slot<BM>(g, slot, wave, lane);
 #pragma unroll
@@ -882,10 +976,11 @@ Plan make_plan(int bm, int M, int KT, int num_n, bool can_split) {
   p.tiles = ((M + bm - 1) / bm) * num_n;
   const int full = p.tiles / cus, tail = p.tiles - full * cus;
   const int upt = KT / unroll_period(KT);
-  // cost is counted in rounds of whole tiles; a 224-row tile has 7/8 of a
-  // 256-row tile's MFMAs, so when both layouts need as many rounds the
-  // shorter tile wins the tie (pick_plan)
-  const float tile_time = 1.0f;
+  // cost is counted in rounds of tiles, a tile's time in units of a 256-row
+  // tile's: a 224-row tile has 7/8 of its MFMAs, plus an epilogue, prologue
+  // and workgroup turnover of about an eighth of a 256-row tile that do not
+  // shrink (measured per tile with cycle counters)
+  const float tile_time = bm == 256 ? 1.0f : 0.89f;
   // a last round at most half full is split; so is a launch with at most
   // half as many tiles as CUs (a short sequence, e.g. an 80- or 160-token
   // text stage): then every tile is cut, so all CUs share the weight stream
@@ -910,11 +1005,18 @@ Plan make_plan(int bm, int M, int KT, int num_n, bool can_split) {
 
 // The 224-row layout (1 x 4 waves) gives a better round count for some M
 // (4,256 tokens x 12 output tiles: 228 tiles in one round, where 256-row tiles
-// need 204 but each is slower); the cheaper plan wins, ties going to the
-// shorter tile.
-Plan pick_plan(int M, int KT, int num_n, bool can_split) {
-  const Plan a = make_plan(224, M, KT, num_n, can_split);
-  const Plan b = make_plan(256, M, KT, num_n, can_split);
+// need 204 but each is slower; the 4,256-token input projection: 19 full
+// 224-row tiles against 17 256-row ones with a 160-row remainder); the
+// cheaper plan wins, ties going to the shorter tile.  `ok` rejects a plan
+// (falling back to the same height without a split) whose split tail would
+// hold q or k tiles: the fix-up's epilogue does not normalize or rotate.
+template <class Ok>
+Plan pick_plan(int M, int KT, int num_n, bool can_split, Ok ok) {
+  auto plan = [&](int bm) {
+    const Plan p = make_plan(bm, M, KT, num_n, can_split);
+    return ok(p) ? p : make_plan(bm, M, KT, num_n, false);
+  };
+  const Plan a = plan(224), b = plan(256);
   return a.cost <= b.cost ? a : b;
 }
 
@@ -925,27 +1027,26 @@ hipError_t launch(GemmArgs g, hipStream_t stream) {
   g.KT = g.K * (F8 ? 1 : 2) / 128;
   Plan p;
   if constexpr (EPI == EPI_IN) {
-    // 256-row tiles only: the q / k epilogue needs a whole head per wave.
     // Split tail tiles end in the fix-up kernel, whose epilogue does not
     // normalize or rotate, so a tail must hold no q or k tile (tail tiles are
     // the last in tile order, i.e. the highest N tiles: MLP ones).
-    p = make_plan(256, g.M, g.KT, g.num_n, can_split);
-    const int num_m = (g.M + 255) / 256;
-    if (p.n_tail && p.n_dp > 0 && (p.n_dp / (GROUP_N * num_m)) * GROUP_N < 2 * g.D / BN)
-      p = make_plan(256, g.M, g.KT, g.num_n, false);
+    const int num_qk = 2 * g.D / BN;
+    p = pick_plan(g.M, g.KT, g.num_n, can_split, [&](const Plan& q) {
+      const int num_m = (g.M + q.bm - 1) / q.bm;
+      return !(q.n_tail && q.n_dp > 0 && (q.n_dp / (GROUP_N * num_m)) * GROUP_N < num_qk);
+    });
     // with every tile split, the fix-up stores q and k as summed, and the
     // norm + RoPE pass runs on them afterwards
     qk_after = p.n_tail > 0 && p.n_dp == 0;
   } else {
-    p = pick_plan(g.M, g.KT, g.num_n, can_split);
+    p = pick_plan(g.M, g.KT, g.num_n, can_split, [](const Plan&) { return true; });
   }
   g.n_dp = p.n_dp;
   g.n_tail = p.n_tail;
   g.n_pieces = p.n_pieces;
   g.unit = unroll_period(g.KT);
   const int grid = g.n_dp + (g.n_tail ? g.n_pieces : 0);
-  const bool tall = EPI == EPI_IN || p.bm == 256;
-  if (tall) {
+  if (p.bm == 256) {
     if (g.unit == 6)
       hipLaunchKernelGGL((gemm_kernel<EPI, 256, 3, F8>), dim3(grid), dim3(256), 0, stream, g);
     else
@@ -953,13 +1054,7 @@ hipError_t launch(GemmArgs g, hipStream_t stream) {
     if (g.n_tail)
       hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 256, F8>), dim3(g.n_tail * 256 * BN / 8 / 256),
                          dim3(256), 0, stream, g);
-    if (qk_after) {
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      return launch_rope4(g.q, g.k, g.pos, g.q_scale, g.k_scale, g.M, g.D / 128, g.theta,
-                          g.qk_eps, stream);
-    }
-  } else if constexpr (EPI == EPI_OUT) {
+  } else {
     if (g.unit == 6)
       hipLaunchKernelGGL((gemm_kernel<EPI, 224, 3, F8>), dim3(grid), dim3(256), 0, stream, g);
     else
@@ -967,6 +1062,12 @@ hipError_t launch(GemmArgs g, hipStream_t stream) {
     if (g.n_tail)
       hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 224, F8>), dim3(g.n_tail * 224 * BN / 8 / 256),
                          dim3(256), 0, stream, g);
+  }
+  if (qk_after) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_rope4(g.q, g.k, g.pos, g.q_scale, g.k_scale, g.M, g.D / 128, g.theta,
+                        g.qk_eps, stream);
   }
   return hipGetLastError();
 }

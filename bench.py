@@ -45,8 +45,8 @@ PEAK_FP8_TFLOPS = 5033.2    # dense fp8 MFMA: twice the bf16 rate
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--weight-sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")

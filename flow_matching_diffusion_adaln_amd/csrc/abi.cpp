@@ -138,7 +138,9 @@ int block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const 
   if ((rc = mark(DIT_STAGE_ROPE))) return rc;
   if ((rc = mark(DIT_STAGE_ATTN))) return rc;
   if ((rc = hip_status(dit::launch_attn(w.q, w.k, w.v, w.cat, s.N, s.H, s.D, s.D + s.F,
-                                        1.0f / sqrtf((float)DIT_HEAD_DIM), stream))))
+                                        1.0f / sqrtf((float)DIT_HEAD_DIM),
+                                        static_cast<const uint16_t*>(q_scale),
+                                        static_cast<const uint16_t*>(k_scale), stream))))
     return rc;
   if ((rc = mark(DIT_STAGE_GEMM_OUT))) return rc;
   if ((rc = hip_status(dit::launch_gemm_out(w.cat, static_cast<const uint16_t*>(w_out), s.N,
@@ -217,7 +219,9 @@ int block_fwd_fp8(const dit_block_desc* desc, const void* x, const void* mod, co
   if ((rc = mark(DIT_STAGE_ROPE))) return rc;
   if ((rc = mark(DIT_STAGE_ATTN))) return rc;
   if ((rc = hip_status(dit::launch_attn(b.q, b.k, b.v, b.cat, s.N, s.H, s.D, s.D + s.F,
-                                        1.0f / sqrtf((float)DIT_HEAD_DIM), stream))))
+                                        1.0f / sqrtf((float)DIT_HEAD_DIM),
+                                        static_cast<const uint16_t*>(q_scale),
+                                        static_cast<const uint16_t*>(k_scale), stream))))
     return rc;
   if ((rc = mark(DIT_STAGE_GEMM_OUT))) return rc;
   // the output projection's input [o | m] is quantized rowwise first
@@ -471,7 +475,8 @@ int dit_attn_fwd(int32_t n_tokens, int32_t n_heads, int32_t head_dim, const void
   return hip_status(dit::launch_attn(static_cast<const uint16_t*>(q),
                                      static_cast<const uint16_t*>(k),
                                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
-                                     n_tokens, n_heads, ld, ld, softmax_scale, stream));
+                                     n_tokens, n_heads, ld, ld, softmax_scale, nullptr,
+                                     nullptr, stream));
 }
 
 int rope4_apply(int32_t n_tokens, int32_t n_heads, int32_t head_dim, void* q, void* k,

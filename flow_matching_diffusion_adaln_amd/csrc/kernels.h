@@ -31,9 +31,12 @@ hipError_t launch_rope4(uint16_t* q, uint16_t* k, const int32_t* pos, const uint
                         const uint16_t* k_scale, int n_tokens, int n_heads, float theta,
                         float eps, hipStream_t stream);
 
+// q_scale / k_scale (both or neither): the QK RMSNorm scales q and k were
+// normalized with; they bound the scores and may let the kernel use a fixed
+// softmax reference instead of a running max.
 hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                        int N, int H, int ld_qkv, int ld_o, float softmax_scale,
-                       hipStream_t stream);
+                       const uint16_t* q_scale, const uint16_t* k_scale, hipStream_t stream);
 
 hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D, int F,
                           uint16_t* q, uint16_t* k, uint16_t* v, uint16_t* cat,

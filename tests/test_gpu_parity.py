@@ -171,6 +171,26 @@ def test_block_parity_qk_scales():
     check_block(configs.C2, seed=4, rows=sample_rows(configs.C2, n_random=24), scaled=True)
 
 
+@pytest.mark.parametrize("g", [1.546875, 1.5625])
+def test_block_parity_score_bound_edges(g):
+    # constant QK-norm scales g: attention's score bound c 128 g^2 (1.01) is
+    # 39.5, just under the 40 that lets the kernel use a fixed softmax
+    # reference (weights then down to about 2^-30), or 40.3, just over it
+    # (running max).  Both must match the oracle.
+    cfg = configs.C1
+    d = inputs.make_block_inputs(cfg, seed=6)
+    d["q_scale"] = inputs.f64_to_bf16_bits(np.full(cfg.head_dim, g))
+    d["k_scale"] = inputs.f64_to_bf16_bits(np.full(cfg.head_dim, g))
+    log(f"block c1 with constant qk scales {g}")
+    dv = to_dev(d)
+    y = widen(run_block(dv, cfg))
+    r = widen(run_block(dv, cfg, flags=ops.DIT_F_NO_RESIDUAL | ops.DIT_F_NO_GATE))
+    ref = oracle_block(d, cfg)
+    ey, er = oracle.rel_l2(y, ref["y"]), oracle.rel_l2(r, ref["r"])
+    log(f"  relL2 y={ey:.3e} r={er:.3e}")
+    assert ey <= TOL_BLOCK and er <= TOL_BLOCK
+
+
 def test_block_parity_ragged_three_streams():
     # 337 tokens: not a multiple of 64, 128 or 256, with all three streams
     check_block(block_config("ragged3", (200, 57, 80), 91))

@@ -11,6 +11,11 @@
 
 namespace {
 
+// The block stores q multiplied by its softmax scale times log2 e (1 /
+// sqrt(128) * log2 e), so attention's fixed-reference path can take exp2 of
+// the raw scores; see launch_attn.
+const float kQMul = (1.0f / sqrtf((float)DIT_HEAD_DIM)) * 1.4426950408889634f;
+
 constexpr size_t kAlign = 256;
 constexpr long long kMaxBytes = 1ll << 32;
 
@@ -133,14 +138,14 @@ int block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const 
   if ((rc = hip_status(dit::launch_gemm_in(
            w.u, static_cast<const uint16_t*>(w_in), s.N, s.D, s.F, w.q, w.k, w.v, w.cat, pos,
            static_cast<const uint16_t*>(q_scale), static_cast<const uint16_t*>(k_scale),
-           desc->rope_theta, desc->qk_eps, w.partial, stream))))
+           desc->rope_theta, desc->qk_eps, kQMul, w.partial, stream))))
     return rc;
   if ((rc = mark(DIT_STAGE_ROPE))) return rc;
   if ((rc = mark(DIT_STAGE_ATTN))) return rc;
   if ((rc = hip_status(dit::launch_attn(w.q, w.k, w.v, w.cat, s.N, s.H, s.D, s.D + s.F,
                                         1.0f / sqrtf((float)DIT_HEAD_DIM),
                                         static_cast<const uint16_t*>(q_scale),
-                                        static_cast<const uint16_t*>(k_scale), stream))))
+                                        static_cast<const uint16_t*>(k_scale), 1, stream))))
     return rc;
   if ((rc = mark(DIT_STAGE_GEMM_OUT))) return rc;
   if ((rc = hip_status(dit::launch_gemm_out(w.cat, static_cast<const uint16_t*>(w_out), s.N,
@@ -213,15 +218,15 @@ int block_fwd_fp8(const dit_block_desc* desc, const void* x, const void* mod, co
   if ((rc = hip_status(dit::launch_gemm_in_fp8(
            w.u8, w.u_scale, static_cast<const uint8_t*>(w_in8), w_in_scale, s.N, s.D, s.F, b.q,
            b.k, b.v, b.cat, pos, static_cast<const uint16_t*>(q_scale),
-           static_cast<const uint16_t*>(k_scale), desc->rope_theta, desc->qk_eps, b.partial,
-           stream))))
+           static_cast<const uint16_t*>(k_scale), desc->rope_theta, desc->qk_eps, kQMul,
+           b.partial, stream))))
     return rc;
   if ((rc = mark(DIT_STAGE_ROPE))) return rc;
   if ((rc = mark(DIT_STAGE_ATTN))) return rc;
   if ((rc = hip_status(dit::launch_attn(b.q, b.k, b.v, b.cat, s.N, s.H, s.D, s.D + s.F,
                                         1.0f / sqrtf((float)DIT_HEAD_DIM),
                                         static_cast<const uint16_t*>(q_scale),
-                                        static_cast<const uint16_t*>(k_scale), stream))))
+                                        static_cast<const uint16_t*>(k_scale), 1, stream))))
     return rc;
   if ((rc = mark(DIT_STAGE_GEMM_OUT))) return rc;
   // the output projection's input [o | m] is quantized rowwise first
@@ -476,7 +481,7 @@ int dit_attn_fwd(int32_t n_tokens, int32_t n_heads, int32_t head_dim, const void
                                      static_cast<const uint16_t*>(k),
                                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
                                      n_tokens, n_heads, ld, ld, softmax_scale, nullptr,
-                                     nullptr, stream));
+                                     nullptr, 0, stream));
 }
 
 int rope4_apply(int32_t n_tokens, int32_t n_heads, int32_t head_dim, void* q, void* k,
@@ -496,7 +501,7 @@ int rope4_apply(int32_t n_tokens, int32_t n_heads, int32_t head_dim, void* q, vo
   return hip_status(dit::launch_rope4(static_cast<uint16_t*>(q), static_cast<uint16_t*>(k), pos,
                                       static_cast<const uint16_t*>(q_scale),
                                       static_cast<const uint16_t*>(k_scale), n_tokens, n_heads,
-                                      theta, qk_eps, stream));
+                                      theta, qk_eps, 1.0f, stream));
 }
 
 int adaln_mod(int32_t n_streams, const int32_t* n_tokens, int32_t width, const void* x,

@@ -31,10 +31,12 @@
 //    and leaves the result unchanged (P and l share the same reference).  P is
 //    rounded to bf16 for the MFMA; one division by the row sum at the end.
 //  * Fixed reference: inside the block, q and k leave the QK RMSNorm with
-//    known scales, which bound every score; when that bound is small (at
-//    most 40 in log2 units, as for scales near one) it serves as the softmax
-//    reference for all tiles, and the row max and rescale checks drop out of
-//    the loop (6-7% of the kernel's time at 4,256 tokens).
+//    known scales, which bound every score, and q is stored already
+//    multiplied by the softmax scale times log2 e.  When the bound is small
+//    (at most 40 in log2 units, as for scales near one) the weights are
+//    exp2 of the raw scores with no reference: the row max, the rescale
+//    checks and the FMA before each exp drop out of the loop (about 10% of
+//    the kernel's time at 4,256 tokens).
 //  * Workgroups of one head are kept on one XCD so its K and V stay in that
 //    XCD's L2.
 #include "common.h"
@@ -100,9 +102,10 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
                                                           const uint16_t* __restrict__ v,
                                                           uint16_t* __restrict__ o, int N,
                                                           int H, int ld_qkv, int ld_o,
-                                                          float c,
+                                                          float c, float c_bound,
                                                           const uint16_t* __restrict__ q_scale,
-                                                          const uint16_t* __restrict__ k_scale) {
+                                                          const uint16_t* __restrict__ k_scale,
+                                                          int prescaled) {
   // distinct arrays per stage: reads of one stage never wait on the
   // direct-to-LDS loads in flight into the other
   __shared__ __attribute__((aligned(16))) uint16_t s_k0[BKEY * HD];
@@ -188,15 +191,17 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
   // Fixed reference.  When q and k come out of the block's QK RMSNorm with
   // scales g_q, g_k, every row has |q| <= sqrt(128) max|g_q| (and likewise
   // for k; RoPE keeps norms, the bf16 rounding adds under 1%), so every
-  // scaled score is at most B = c 128 max|g_q| max|g_k| (1.01 for the
-  // rounding).  With B <= 40 the reference m = B needs no running max at
-  // all: P = exp2(S c - B) <= 1, and even the largest weight of a row is at
-  // least 2^-80, far inside fp32 and bf16 range, so P, the row sums and O
-  // keep full relative precision.  The row max and the rescale checks drop
-  // out of the loop.  Larger bounds, and attention without scales, use the
-  // running max.
+  // scaled score S c lies within +-B, B = c 128 max|g_q| max|g_k| (1.01 for
+  // the rounding; c = c_bound, the softmax scale times log2 e).  The block
+  // stores q already multiplied by c (prescaled; then c = 1 here), and with
+  // B <= 40 the kernel takes P = exp2(S) with no reference at all: the
+  // weights lie in [2^-40, 2^40], far inside fp32 and bf16 range, the row
+  // sums stay below 2^57, and the normalization at the end cancels the
+  // common factor.  The FMA before each exp, the row max and the rescale
+  // checks drop out of the loop.  Larger bounds, and attention without
+  // scales, use the running max.
   bool fixed = false;
-  if (q_scale != nullptr) {
+  if (q_scale != nullptr && prescaled) {
     float gq = fmaxf(fabsf(bf2f(q_scale[lane])), fabsf(bf2f(q_scale[lane + 64])));
     float gk = fmaxf(fabsf(bf2f(k_scale[lane])), fabsf(bf2f(k_scale[lane + 64])));
 #pragma unroll
@@ -204,9 +209,8 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
       gq = fmaxf(gq, __shfl_xor(gq, off, 64));
       gk = fmaxf(gk, __shfl_xor(gk, off, 64));
     }
-    const float bound = c * 128.0f * gq * gk * 1.01f;
+    const float bound = c_bound * 128.0f * gq * gk * 1.01f;
     fixed = bound <= 40.0f;  // false for NaN: the running max then
-    if (fixed) m_run = bound;
   }
 
   // S^T = K Q^T for one key tile: 2 key blocks of 32, 8 k steps of 16 dims.
@@ -254,13 +258,15 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
   };
   // P = exp2(S c - m) in bf16 for the PV MFMA; with `lim` < 64 keys at local
   // index >= lim get no weight (the last tile of a ragged N)
-  auto softmax = [&](const f32x16 (&sc)[2], bf16x8 (&pb)[4], int lim) __attribute__((always_inline)) {
+  auto softmax = [&](auto fixed_t, const f32x16 (&sc)[2], bf16x8 (&pb)[4], int lim)
+      __attribute__((always_inline)) {
+    constexpr bool FIXED = decltype(fixed_t)::value;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, -m_run));
+        float p = __builtin_amdgcn_exp2f(FIXED ? sc[kb][r] : fmaf(sc[kb][r], c, -m_run));
         if (lim < BKEY && 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7) >= lim) p = 0.f;
         psum += p;
         pb[2 * kb + (r >> 3)][r & 7] = (__bf16)p;
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
       resc(mx_cur);
       // step 1: S(t + 1) MFMAs with softmax(t) VALU
       qk(ring_k[sl ^ 1], nxt);
-      softmax(cur, pb, BKEY);
+      softmax(fixed_t, cur, pb, BKEY);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // first K fragment
   #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -362,7 +368,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
     auto last = [&](auto slot, f32x16 (&cur)[2], float mx_cur) __attribute__((always_inline)) {
       constexpr int sl = decltype(slot)::value;
       resc(mx_cur);
-      softmax(cur, pb, N - (ntiles - 1) * BKEY);
+      softmax(fixed_t, cur, pb, N - (ntiles - 1) * BKEY);
       pv(ring_v[sl], pb);
     };
     int t = 0;
@@ -402,10 +408,12 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
 
 hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                        int N, int H, int ld_qkv, int ld_o, float softmax_scale,
-                       const uint16_t* q_scale, const uint16_t* k_scale, hipStream_t stream) {
+                       const uint16_t* q_scale, const uint16_t* k_scale, int q_prescaled,
+                       hipStream_t stream) {
   const int nqt = (N + BQ - 1) / BQ;
+  const float c = softmax_scale * DIT_LOG2E;
   hipLaunchKernelGGL(attn_fwd_kernel, dim3(nqt * H), dim3(64 * NWAVE), 0, stream, q, k, v, o, N, H,
-                     ld_qkv, ld_o, softmax_scale * DIT_LOG2E, q_scale, k_scale);
+                     ld_qkv, ld_o, q_prescaled ? 1.0f : c, c, q_scale, k_scale, q_prescaled);
   return hipGetLastError();
 }
 

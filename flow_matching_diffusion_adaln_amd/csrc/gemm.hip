@@ -72,6 +72,7 @@ struct GemmArgs {
   const uint16_t* k_scale;  // [128] bf16
   float qk_eps;
   float theta;
+  float q_mul;             // multiplies the normalized, rotated q before it is stored
   double rope_rev[16];     // theta^(-2j / 32) / (2 pi): turns per position step of pair j
   // output projection
   const uint16_t* x;  // residual [M, D]
@@ -275,6 +276,7 @@ __device__ __forceinline__ void epilogue_qk(const GemmArgs& g, const f32x16 (&ac
   uint16_t* const dst = which ? g.k : g.q;
   const uint16_t* const scale = which ? g.k_scale : g.q_scale;
   const int c0 = tn * BN - which * g.D + wn * NB * 32;  // first dim of the head
+  const float qmul = which ? 1.0f : g.q_mul;
   // Per-lane inputs, all loads issued before the first use: the scale of
   // this lane's 64 dims, the turn rate of its 8 pairs per axis, and the
   // positions of its 4 rows.
@@ -307,7 +309,7 @@ __device__ __forceinline__ void epilogue_qk(const GemmArgs& g, const f32x16 (&ac
 #pragma unroll
       for (int r = 0; r < 16; ++r) ss = fmaf(acc[i][j][r], acc[i][j][r], ss);
     ss += __shfl_xor(ss, 32, 64);
-    const float rstd = rsqrtf(ss * (1.0f / 128.0f) + g.qk_eps);
+    const float rstd = rsqrtf(ss * (1.0f / 128.0f) + g.qk_eps) * qmul;
     if (row >= g.M) continue;
     const int pa[4] = {p4[i].x, p4[i].y, p4[i].z, p4[i].w};
 #pragma unroll
@@ -356,6 +358,7 @@ __device__ __forceinline__ void epilogue_qk224(const GemmArgs& g, const f32x16 (
   const uint16_t* const scale = which ? g.k_scale : g.q_scale;
   const int hh = wn & 1;                                  // half of the head
   const int c0 = tn * BN - which * g.D + wn * NB * 32;    // first dim of this wave
+  const float qmul = which ? 1.0f : g.q_mul;
   uint2 gsc[NB][4];
 #pragma unroll
   for (int j = 0; j < NB; ++j)
@@ -392,7 +395,7 @@ __device__ __forceinline__ void epilogue_qk224(const GemmArgs& g, const f32x16 (
   for (int i = 0; i < MB; ++i) {
     const int row = tm * BM + i * 32 + ln;
     const float tot = ss[i] + s_rs[(wn ^ 1) * BM + i * 32 + ln];
-    const float rstd = rsqrtf(tot * (1.0f / 128.0f) + g.qk_eps);
+    const float rstd = rsqrtf(tot * (1.0f / 128.0f) + g.qk_eps) * qmul;
     if (row >= g.M) continue;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -1067,7 +1070,7 @@ hipError_t launch(GemmArgs g, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_rope4(g.q, g.k, g.pos, g.q_scale, g.k_scale, g.M, g.D / 128, g.theta,
-                        g.qk_eps, stream);
+                        g.qk_eps, g.q_mul, stream);
   }
   return hipGetLastError();
 }
@@ -1084,6 +1087,7 @@ GemmArgs in_args(const void* u, const void* w_in, int M, int D, int F, uint16_t*
   g.q_scale = q_scale;
   g.k_scale = k_scale;
   g.qk_eps = qk_eps;
+  g.q_mul = 1.0f;
   g.theta = theta;
   const double two_pi = 6.283185307179586;
   for (int j = 0; j < 16; ++j) g.rope_rev[j] = pow((double)theta, -2.0 * j / 32.0) / two_pi;
@@ -1128,10 +1132,12 @@ GemmArgs out_args(const void* cat, const void* w_out, int M, int D, int F, const
 hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D, int F,
                           uint16_t* q, uint16_t* k, uint16_t* v, uint16_t* cat,
                           const int32_t* pos, const uint16_t* q_scale, const uint16_t* k_scale,
-                          float theta, float qk_eps, float* partial, hipStream_t stream) {
-  return launch<EPI_IN, false>(in_args(u, w_in, M, D, F, q, k, v, cat, pos, q_scale, k_scale,
-                                       theta, qk_eps, partial),
-                               stream);
+                          float theta, float qk_eps, float q_mul, float* partial,
+                          hipStream_t stream) {
+  GemmArgs g = in_args(u, w_in, M, D, F, q, k, v, cat, pos, q_scale, k_scale, theta, qk_eps,
+                       partial);
+  g.q_mul = q_mul;
+  return launch<EPI_IN, false>(g, stream);
 }
 
 hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, int D, int F,
@@ -1145,9 +1151,10 @@ hipError_t launch_gemm_in_fp8(const uint8_t* u8, const float* u_scale, const uin
                               const float* w_in_scale, int M, int D, int F, uint16_t* q,
                               uint16_t* k, uint16_t* v, uint16_t* cat, const int32_t* pos,
                               const uint16_t* q_scale, const uint16_t* k_scale, float theta,
-                              float qk_eps, float* partial, hipStream_t stream) {
+                              float qk_eps, float q_mul, float* partial, hipStream_t stream) {
   GemmArgs g = in_args(u8, w_in8, M, D, F, q, k, v, cat, pos, q_scale, k_scale, theta, qk_eps,
                        partial);
+  g.q_mul = q_mul;
   g.sa = u_scale;
   g.sw = w_in_scale;
   return launch<EPI_IN, true>(g, stream);

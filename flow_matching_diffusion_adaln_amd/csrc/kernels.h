@@ -27,21 +27,27 @@ hipError_t launch_adaln_fp8(const uint16_t* x, const uint16_t* mod, uint8_t* q8,
 hipError_t launch_quant_rows(const uint16_t* x, uint8_t* q, float* scale, int M, int K,
                              hipStream_t stream);
 
+// q_mul multiplies q after the norm and rotation (1 for plain RoPE; the
+// block passes the softmax's log2 e / sqrt(d), see launch_attn)
 hipError_t launch_rope4(uint16_t* q, uint16_t* k, const int32_t* pos, const uint16_t* q_scale,
                         const uint16_t* k_scale, int n_tokens, int n_heads, float theta,
-                        float eps, hipStream_t stream);
+                        float eps, float q_mul, hipStream_t stream);
 
 // q_scale / k_scale (both or neither): the QK RMSNorm scales q and k were
-// normalized with; they bound the scores and may let the kernel use a fixed
-// softmax reference instead of a running max.
+// normalized with.  q_prescaled: q already carries softmax_scale * log2 e.
+// With both, the scores are bounded and the kernel may use a fixed softmax
+// reference, P = exp2(q k), instead of a running max.
 hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                        int N, int H, int ld_qkv, int ld_o, float softmax_scale,
-                       const uint16_t* q_scale, const uint16_t* k_scale, hipStream_t stream);
+                       const uint16_t* q_scale, const uint16_t* k_scale, int q_prescaled,
+                       hipStream_t stream);
 
+// q_mul multiplies the normalized, rotated q before it is stored
 hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D, int F,
                           uint16_t* q, uint16_t* k, uint16_t* v, uint16_t* cat,
                           const int32_t* pos, const uint16_t* q_scale, const uint16_t* k_scale,
-                          float theta, float qk_eps, float* partial, hipStream_t stream);
+                          float theta, float qk_eps, float q_mul, float* partial,
+                          hipStream_t stream);
 
 hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, int D, int F,
                            const uint16_t* x, const uint16_t* mod, uint16_t* y, int e0, int e1,
@@ -53,7 +59,7 @@ hipError_t launch_gemm_in_fp8(const uint8_t* u8, const float* u_scale, const uin
                               const float* w_in_scale, int M, int D, int F, uint16_t* q,
                               uint16_t* k, uint16_t* v, uint16_t* cat, const int32_t* pos,
                               const uint16_t* q_scale, const uint16_t* k_scale, float theta,
-                              float qk_eps, float* partial, hipStream_t stream);
+                              float qk_eps, float q_mul, float* partial, hipStream_t stream);
 
 hipError_t launch_gemm_out_fp8(const uint8_t* cat8, const float* cat_scale,
                                const uint8_t* w_out8, const float* w_out_scale, int M, int D,

@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void rope4_kernel(uint16_t* __restrict__ q,
                                                     const uint16_t* __restrict__ q_scale,
                                                     const uint16_t* __restrict__ k_scale,
                                                     int n_tokens, int n_heads, double log2_theta,
-                                                    float eps, int do_norm) {
+                                                    float eps, int do_norm, float q_mul) {
   const int lane = threadIdx.x & 63;
   const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (tok >= n_tokens) return;
@@ -81,10 +81,11 @@ __global__ __launch_bounds__(256) void rope4_kernel(uint16_t* __restrict__ q,
 #pragma unroll
       for (int t = 0; t < 8; ++t) e[t] = e[t] * r * g[which][t];
     }
+    const float mul = which ? 1.0f : q_mul;
     uint32_t o[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const float x0 = e[2 * t], x1 = e[2 * t + 1];
+      const float x0 = e[2 * t] * mul, x1 = e[2 * t + 1] * mul;
       o[t] = pack2(x0 * cs[t] - x1 * sn[t], x0 * sn[t] + x1 * cs[t]);
     }
     *ptr = make_uint4(o[0], o[1], o[2], o[3]);
@@ -93,10 +94,11 @@ __global__ __launch_bounds__(256) void rope4_kernel(uint16_t* __restrict__ q,
 
 hipError_t launch_rope4(uint16_t* q, uint16_t* k, const int32_t* pos, const uint16_t* q_scale,
                         const uint16_t* k_scale, int n_tokens, int n_heads, float theta,
-                        float eps, hipStream_t stream) {
+                        float eps, float q_mul, hipStream_t stream) {
   const int do_norm = q_scale != nullptr;
   hipLaunchKernelGGL(rope4_kernel, dim3((n_tokens + 3) / 4), dim3(256), 0, stream, q, k, pos,
-                     q_scale, k_scale, n_tokens, n_heads, log2((double)theta), eps, do_norm);
+                     q_scale, k_scale, n_tokens, n_heads, log2((double)theta), eps, do_norm,
+                     q_mul);
   return hipGetLastError();
 }
 

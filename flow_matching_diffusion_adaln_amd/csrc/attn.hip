@@ -35,8 +35,9 @@
 //    multiplied by the softmax scale times log2 e.  When the bound is small
 //    (at most 40 in log2 units, as for scales near one) the weights are
 //    exp2 of the raw scores with no reference: the row max, the rescale
-//    checks and the FMA before each exp drop out of the loop (about 10% of
-//    the kernel's time at 4,256 tokens).
+//    checks and the FMA before each exp drop out of the loop.  Each tile's
+//    softmax is then split in halves over both MFMA steps (see run_fixed).
+//    Together about 20% of the kernel's time at 4,256 tokens.
 //  * Workgroups of one head are kept on one XCD so its K and V stay in that
 //    XCD's L2.
 #include "common.h"
@@ -258,15 +259,14 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
   };
   // P = exp2(S c - m) in bf16 for the PV MFMA; with `lim` < 64 keys at local
   // index >= lim get no weight (the last tile of a ragged N)
-  auto softmax = [&](auto fixed_t, const f32x16 (&sc)[2], bf16x8 (&pb)[4], int lim)
+  auto softmax = [&](const f32x16 (&sc)[2], bf16x8 (&pb)[4], int lim)
       __attribute__((always_inline)) {
-    constexpr bool FIXED = decltype(fixed_t)::value;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(FIXED ? sc[kb][r] : fmaf(sc[kb][r], c, -m_run));
+        float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, -m_run));
         if (lim < BKEY && 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7) >= lim) p = 0.f;
         psum += p;
         pb[2 * kb + (r >> 3)][r & 7] = (__bf16)p;
@@ -293,16 +293,8 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
     }
   };
 
-  // the key loop, instantiated with and without the fixed reference
-  auto run = [&](auto fixed_t) __attribute__((always_inline)) {
-    constexpr bool FIXED = decltype(fixed_t)::value;
-    auto rmax = [&](const f32x16 (&sc)[2]) __attribute__((always_inline)) {
-      if constexpr (FIXED) return 0.f;
-      else return row_max(sc);
-    };
-    auto resc = [&](float mx) __attribute__((always_inline)) {
-      if constexpr (!FIXED) rescale(mx);
-    };
+  // the key loop with the running max
+  auto run_online = [&]() __attribute__((always_inline)) {
     // Software pipeline over key tiles.  Iteration t holds S(t) and its row
     // max; it computes S(t + 1) = K(t + 1) Q^T while the softmax of S(t) runs
     // (MFMA and VALU of one wave overlap), then O += V(t) P(t) while the row
@@ -324,7 +316,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
     __builtin_amdgcn_s_waitcnt(vmcnt_imm_lpw());
     barrier_keep_loads();
     qk(s_k0, sa);
-    mx_a = rmax(sa);
+    mx_a = row_max(sa);
     dma_v(1, s_v1);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm_lpw());
     barrier_keep_loads();
@@ -336,10 +328,10 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
     auto iter = [&](auto slot, int t, f32x16 (&cur)[2], float mx_cur, f32x16 (&nxt)[2],
                     float& mx_nxt) __attribute__((always_inline)) {
       constexpr int sl = decltype(slot)::value;
-      resc(mx_cur);
+      rescale(mx_cur);
       // step 1: S(t + 1) MFMAs with softmax(t) VALU
       qk(ring_k[sl ^ 1], nxt);
-      softmax(fixed_t, cur, pb, BKEY);
+      softmax(cur, pb, BKEY);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // first K fragment
   #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -352,7 +344,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
       dma_k(t + 3, ring_k[sl ^ 1]);
       // step 2: O += V(t) P(t) with the row max of S(t + 1)
       pv(ring_v[sl], pb);
-      mx_nxt = rmax(nxt);
+      mx_nxt = row_max(nxt);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // first V fragment
   #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -367,8 +359,8 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
     };
     auto last = [&](auto slot, f32x16 (&cur)[2], float mx_cur) __attribute__((always_inline)) {
       constexpr int sl = decltype(slot)::value;
-      resc(mx_cur);
-      softmax(fixed_t, cur, pb, N - (ntiles - 1) * BKEY);
+      rescale(mx_cur);
+      softmax(cur, pb, N - (ntiles - 1) * BKEY);
       pv(ring_v[sl], pb);
     };
     int t = 0;
@@ -383,10 +375,121 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
       last(std::integral_constant<int, 0>{}, sa, mx_a);
     }
   };
+  // The loop with the fixed reference.  With no running max a tile's
+  // weights need nothing but its own scores, so the softmax of each tile is
+  // split in its two 32-key halves: the second half of P(t) is computed in
+  // step 1 beside the QK MFMAs of tile t + 1, the first half of P(t + 1) in
+  // step 2 beside the PV MFMAs of tile t (which read the other register set
+  // of first halves).  Both steps then carry VALU work under their MFMAs.
+  // The first half of the last tile takes the ragged-N mask in the iteration
+  // before it (MASK0), its second half in the peeled last step.
+  auto run_fixed = [&]() __attribute__((always_inline)) {
+    uint16_t* const ring_k[2] = {s_k0, s_k1};
+    uint16_t* const ring_v[2] = {s_v0, s_v1};
+    const int lim = N - (ntiles - 1) * BKEY;
+    // weights of one 32-key half (kb) of a tile into its two B fragments;
+    // keys at tile index >= lim get none.  Returns the half's row sum.
+    auto half = [&](const f32x16& sv, int kb, bf16x8 (&ph)[2], int lm)
+        __attribute__((always_inline)) {
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(sv[r]);
+        if (lm < BKEY && 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7) >= lm) p = 0.f;
+        sum += p;
+        ph[r >> 3][r & 7] = (__bf16)p;
+      }
+      return sum;
+    };
+    auto pv2 = [&](const uint16_t* sv, const bf16x8 (&p0)[2], const bf16x8 (&p1)[2])
+        __attribute__((always_inline)) {
+      const char* svb = reinterpret_cast<const char*>(sv);
+      bf16x8 fv[2];
+      fv[0] = vfrag(svb, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i + 1 < 16) fv[(i + 1) & 1] = vfrag(svb, i + 1);
+        const bf16x8& pf = (i >> 3) ? p1[(i >> 2) & 1] : p0[(i >> 2) & 1];
+        acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[i & 1], pf, acc[i & 3], 0, 0, 0);
+      }
+    };
+    f32x16 sa[2], sb[2];
+    bf16x8 pa0[2], pb0[2], p1[2];
+
+    dma_k(0, s_k0);
+    dma_v(0, s_v0);
+    dma_k(1, s_k1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm_lpw());
+    barrier_keep_loads();
+    qk(s_k0, sa);
+    l_run = half(sa[0], 0, pa0, ntiles == 1 ? lim : BKEY);
+    dma_v(1, s_v1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm_lpw());
+    barrier_keep_loads();
+    dma_k(2, s_k0);
+
+    auto iter = [&](auto slot, auto mask0, int t, f32x16 (&cur)[2], f32x16 (&nxt)[2],
+                    bf16x8 (&p0_cur)[2], bf16x8 (&p0_nxt)[2]) __attribute__((always_inline)) {
+      constexpr int sl = decltype(slot)::value;
+      constexpr bool MASK0 = decltype(mask0)::value;
+      // step 1: S(t + 1) MFMAs with the second half of P(t)
+      qk(ring_k[sl ^ 1], nxt);
+      l_run += half(cur[1], 1, p1, BKEY);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // first K fragment
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next K fragment
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      barrier_keep_loads();  // B1
+      dma_k(t + 3, ring_k[sl ^ 1]);
+      // step 2: O += V(t) P(t) with the first half of P(t + 1)
+      pv2(ring_v[sl], p0_cur, p1);
+      l_run += half(nxt[0], 0, p0_nxt, MASK0 ? lim : BKEY);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // first V fragment
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next V fragment
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm_lpw());
+      barrier_keep_loads();  // B2
+      dma_v(t + 2, ring_v[sl]);
+    };
+    auto last = [&](auto slot, f32x16 (&cur)[2], bf16x8 (&p0_cur)[2])
+        __attribute__((always_inline)) {
+      constexpr int sl = decltype(slot)::value;
+      l_run += half(cur[1], 1, p1, lim);
+      pv2(ring_v[sl], p0_cur, p1);
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using NoMask = std::false_type;
+    using Mask = std::true_type;
+    int t = 0;
+    for (; t + 3 < ntiles; t += 2) {
+      iter(S0{}, NoMask{}, t, sa, sb, pa0, pb0);
+      iter(S1{}, NoMask{}, t + 1, sb, sa, pb0, pa0);
+    }
+    if (t + 3 == ntiles) {
+      iter(S0{}, NoMask{}, t, sa, sb, pa0, pb0);
+      iter(S1{}, Mask{}, t + 1, sb, sa, pb0, pa0);
+      last(S0{}, sa, pa0);
+    } else if (t + 2 == ntiles) {
+      iter(S0{}, Mask{}, t, sa, sb, pa0, pb0);
+      last(S1{}, sb, pb0);
+    } else {
+      last(S0{}, sa, pa0);
+    }
+  };
   if (fixed)
-    run(std::true_type{});
+    run_fixed();
   else
-    run(std::false_type{});
+    run_online();
   __builtin_amdgcn_s_waitcnt(vmcnt_imm0());
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);

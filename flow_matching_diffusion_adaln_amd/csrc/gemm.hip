@@ -921,13 +921,32 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
   const int g0 = ((i * NB + 2 * jp) * 4 + rr) * 64;  // group offsets in float4
   const int g1 = g0 + 4 * 64;
   float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int p = pa; p <= pb; ++p) {
-    // the tile is a piece's second item when the piece began in an earlier tile
-    const int slot = 2 * p + (piece_start(p, units, g.n_pieces) < ua ? 1 : 0);
-    const float4* src = partial_slot<BM>(g, slot, wave, lane);
-    const float4 va = src[g0], vb = src[g1];
-    a[0] += va.x; a[1] += va.y; a[2] += va.z; a[3] += va.w;
-    b[0] += vb.x; b[1] += vb.y; b[2] += vb.z; b[3] += vb.w;
+  // The pieces' partials are independent loads: up to FIX_BATCH of them are
+  // issued before they are summed (one at a time, the sum would wait one L2
+  // round trip per piece).  They are added in piece order, as one at a time.
+  constexpr int FIX_BATCH = 8;
+  const int pa_second = piece_start(pa, units, g.n_pieces) < ua ? 1 : 0;
+  for (int p0 = pa; p0 <= pb; p0 += FIX_BATCH) {
+    float4 va[FIX_BATCH], vb[FIX_BATCH];
+#pragma unroll
+    for (int u = 0; u < FIX_BATCH; ++u) {
+      const int p = p0 + u;
+      va[u] = vb[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (p <= pb) {
+        // the tile is a piece's second item when the piece began in an
+        // earlier tile, which only the first piece pa can have done
+        const int slot = 2 * p + (p == pa ? pa_second : 0);
+        const float4* src = partial_slot<BM>(g, slot, wave, lane);
+        va[u] = src[g0];
+        vb[u] = src[g1];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < FIX_BATCH; ++u) {
+      if (p0 + u > pb) break;
+      a[0] += va[u].x; a[1] += va[u].y; a[2] += va[u].z; a[3] += va[u].w;
+      b[0] += vb[u].x; b[1] += vb[u].y; b[2] += vb[u].z; b[3] += vb[u].w;
+    }
   }
   if constexpr (F8) {
     const int ln = lane & 31, hl = lane >> 5;

@@ -343,15 +343,16 @@ __device__ __forceinline__ void epilogue_qk(const GemmArgs& g, const f32x16 (&ac
   store_staged<16>(st, MB * 32, dst + c0, g.D, tm * BM + wm * MB * 32, g.M, lane);
 }
 
-// q / k tile epilogue of the 224-row layout (1 x 4 waves of 224 x 64): a
-// head's 128 dims are split over waves wn and wn ^ 1, 64 each, so the two
-// halves of each row's sum of squares meet in LDS (s_rs, 224 floats per
+// q / k tile epilogue of the 1 x 4 layouts (224 or 128 rows; waves of
+// BM x 64): a head's 128 dims are split over waves wn and wn ^ 1, 64 each, so
+// the two halves of each row's sum of squares meet in LDS (s_rs, BM floats per
 // wave).  Wave wn holds axes 2 (wn & 1) and 2 (wn & 1) + 1 in its blocks 0
 // and 1; the rest is the 256-row epilogue's norm and rotation.
-__device__ __forceinline__ void epilogue_qk224(const GemmArgs& g, const f32x16 (&acc)[7][2],
-                                               int tm, int tn, int wn, int lane, char* st,
-                                               float* s_rs) {
-  constexpr int BM = 224, MB = 7, NB = 2;
+template <int BM>
+__device__ __forceinline__ void epilogue_qk224(const GemmArgs& g,
+                                               const f32x16 (&acc)[BM / 32][2], int tm, int tn,
+                                               int wn, int lane, char* st, float* s_rs) {
+  constexpr int MB = BM / 32, NB = 2;
   const int ln = lane & 31, hl = lane >> 5;
   const int which = tn * BN / g.D;  // 0: q, 1: k
   uint16_t* const dst = which ? g.k : g.q;
@@ -511,7 +512,7 @@ __device__ __forceinline__ void epilogue_in(const GemmArgs& g,
     if constexpr (BM == 256)
       epilogue_qk(g, acc, tm, tn, wm, wn, lane, st);
     else
-      epilogue_qk224(g, acc, tm, tn, wn, lane, st, s_rs);
+      epilogue_qk224<BM>(g, acc, tm, tn, wn, lane, st, s_rs);
     return;
   }
   const int row0 = tm * BM + wm * MB * 32;
@@ -631,8 +632,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t s_a2[NA == 3 ? BM * BK : 8];
   __shared__ __attribute__((aligned(16))) uint16_t s_w0[BN * BK];
   __shared__ __attribute__((aligned(16))) uint16_t s_w1[BN * BK];
-  // row sums of squares exchanged by the 224-row q / k epilogue
-  __shared__ float s_rs[EPI == EPI_IN && BM == 224 ? 4 * 224 : 1];
+  // row sums of squares exchanged by the q / k epilogue of the 1 x 4 layout
+  __shared__ float s_rs[EPI == EPI_IN && BM != 256 ? 4 * BM : 1];
   uint16_t* const ring_a[3] = {s_a0, s_a1, s_a2};
   uint16_t* const ring_w[NW] = {s_w0, s_w1};
 
@@ -844,7 +845,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     if constexpr (!SPLIT) {
       if constexpr (F8) scale_acc<EPI, BM>(g, acc, tm, tn, wm, wn, lane);
       // every wave is past its last fragment read of the ring before any
-      // wave stages into it; wave w stages into ring array w (>= 28 KB)
+      // wave stages into it; wave w stages into ring array w (>= 16 KB, as
+      // much as a wave stages)
       __syncthreads();
       char* const st = reinterpret_cast<char*>(wave == 0   ? s_a0
                                                : wave == 1 ? s_a1
@@ -1002,7 +1004,7 @@ Plan make_plan(int bm, int M, int KT, int num_n, bool can_split) {
   // tile's: a 224-row tile has 7/8 of its MFMAs, plus an epilogue, prologue
   // and workgroup turnover of about an eighth of a 256-row tile that do not
   // shrink (measured per tile with cycle counters)
-  const float tile_time = bm == 256 ? 1.0f : 0.89f;
+  const float tile_time = bm == 256 ? 1.0f : bm == 224 ? 0.89f : 0.56f;
   // a last round at most half full is split; so is a launch with at most
   // half as many tiles as CUs (a short sequence, e.g. an 80- or 160-token
   // text stage): then every tile is cut, so all CUs share the weight stream
@@ -1032,14 +1034,26 @@ Plan make_plan(int bm, int M, int KT, int num_n, bool can_split) {
 // cheaper plan wins, ties going to the shorter tile.  `ok` rejects a plan
 // (falling back to the same height without a split) whose split tail would
 // hold q or k tiles: the fix-up's epilogue does not normalize or rotate.
+//
+// 128-row tiles (1 x 4 waves of 128 x 64) serve sequences of at most 128
+// tokens when every tile is split (an 80-token text block: one row of tiles,
+// where a 224-row tile would run 2.8 times the MFMAs the 80 rows need).
+// Their whole-tile epilogues are then never used; bf16 only.  For longer
+// sequences they were measured slower than 224-row tiles (336 tokens, output
+// projection: more tiles with the same fixed costs each).
 template <class Ok>
-Plan pick_plan(int M, int KT, int num_n, bool can_split, Ok ok) {
+Plan pick_plan(int M, int KT, int num_n, bool can_split, bool allow128, Ok ok) {
   auto plan = [&](int bm) {
     const Plan p = make_plan(bm, M, KT, num_n, can_split);
     return ok(p) ? p : make_plan(bm, M, KT, num_n, false);
   };
   const Plan a = plan(224), b = plan(256);
-  return a.cost <= b.cost ? a : b;
+  Plan best = a.cost <= b.cost ? a : b;
+  if (allow128 && can_split && M <= 128) {
+    const Plan c = make_plan(128, M, KT, num_n, true);
+    if (c.n_dp == 0 && c.n_tail > 0 && ok(c) && c.cost < best.cost) best = c;
+  }
+  return best;
 }
 
 template <int EPI, bool F8>
@@ -1053,7 +1067,7 @@ hipError_t launch(GemmArgs g, hipStream_t stream) {
     // normalize or rotate, so a tail must hold no q or k tile (tail tiles are
     // the last in tile order, i.e. the highest N tiles: MLP ones).
     const int num_qk = 2 * g.D / BN;
-    p = pick_plan(g.M, g.KT, g.num_n, can_split, [&](const Plan& q) {
+    p = pick_plan(g.M, g.KT, g.num_n, can_split, !F8, [&](const Plan& q) {
       const int num_m = (g.M + q.bm - 1) / q.bm;
       return !(q.n_tail && q.n_dp > 0 && (q.n_dp / (GROUP_N * num_m)) * GROUP_N < num_qk);
     });
@@ -1061,7 +1075,7 @@ hipError_t launch(GemmArgs g, hipStream_t stream) {
     // norm + RoPE pass runs on them afterwards
     qk_after = p.n_tail > 0 && p.n_dp == 0;
   } else {
-    p = pick_plan(g.M, g.KT, g.num_n, can_split, [](const Plan&) { return true; });
+    p = pick_plan(g.M, g.KT, g.num_n, can_split, !F8, [](const Plan&) { return true; });
   }
   g.n_dp = p.n_dp;
   g.n_tail = p.n_tail;
@@ -1076,6 +1090,15 @@ hipError_t launch(GemmArgs g, hipStream_t stream) {
     if (g.n_tail)
       hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 256, F8>), dim3(g.n_tail * 256 * BN / 8 / 256),
                          dim3(256), 0, stream, g);
+  } else if (p.bm == 128) {
+    if constexpr (!F8) {
+      if (g.unit == 6)
+        hipLaunchKernelGGL((gemm_kernel<EPI, 128, 3, false>), dim3(grid), dim3(256), 0, stream, g);
+      else
+        hipLaunchKernelGGL((gemm_kernel<EPI, 128, 2, false>), dim3(grid), dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((gemm_fixup_kernel<EPI, 128, false>), dim3(g.n_tail * 128 * BN / 8 / 256),
+                         dim3(256), 0, stream, g);
+    }
   } else {
     if (g.unit == 6)
       hipLaunchKernelGGL((gemm_kernel<EPI, 224, 3, F8>), dim3(grid), dim3(256), 0, stream, g);

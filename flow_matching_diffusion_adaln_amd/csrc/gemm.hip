@@ -15,7 +15,8 @@
 //    gate per stream, "How it works": scale, shift and gate per stream).
 //
 // Tiling for gfx950: BM x 256 workgroup tiles with BM = 256 (4 waves in
-// 2 x 2, 128 x 128 each) or BM = 224 (4 waves in 1 x 4, 224 x 64 each), built
+// 2 x 2, 128 x 128 each) or BM = 224 (4 waves in 1 x 4, 224 x 64 each), and
+// BM = 128 (1 x 4, 128 x 64) for split launches of at most 128 rows, built
 // from v_mfma_f32_32x32x16_bf16 blocks with the fp32 accumulators in AGPRs.
 // The host picks the tile height: fewest rounds of tiles over the CUs, then
 // the shorter tile (224 divides the 4,256-token sequence into 19 tiles, 256

@@ -200,6 +200,14 @@ def test_block_parity_single_token():
     check_block(block_config("one", (1,), 92))
 
 
+# At most 128 tokens the projections run 128-row tiles, every tile split
+# along K: exactly one full row of tiles (128), a last 32-row block that is
+# only partly inside M (97), and two streams (100 image + 28 text).
+@pytest.mark.parametrize("n_tokens,cid", [((128,), 97), ((97,), 98), ((100, 28), 99)])
+def test_block_parity_short_128_row_tiles(n_tokens, cid):
+    check_block(block_config(f"short{sum(n_tokens)}", n_tokens, cid))
+
+
 # On a 256-CU device these token counts make the GEMMs cut their last, partly
 # filled round of tiles along K (fp32 partial tiles + a fix-up pass):
 #   513:   input projection (3 x 108 tiles of 256 rows), 1 round + 68 tiles

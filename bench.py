@@ -552,7 +552,6 @@ def main():
         },
         "gemm_out_tflops": round(gemm_out_flop / (st["gemm_out"] * 1e-3) / 1e12, 2),
         "adaln_gbs": round(4.0 * cfg.N * D / (st["adaln"] * 1e-3) / 1e9, 1),
-        "rope_gbs": round(8.0 * cfg.N * D / (st["rope"] * 1e-3) / 1e9, 1),
         "roofline": {
             "kernel": "input projection: gemm_kernel<EPI_IN> (q|k|v|SwiGLU, QK RMSNorm + RoPE "
                       "epilogue) + its split-tail fix-up, timed together",

@@ -63,12 +63,5 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-def device_asm(src: str, out: str) -> None:
-    """Write the gfx950 assembly of one source (for inspecting register use)."""
-    cmd = [hipcc(), "-x", "hip", "-S", "--cuda-device-only", os.path.join(CSRC, src),
-           "-o", out] + compile_flags()
-    subprocess.run(cmd, check=True)
-
-
 if __name__ == "__main__":
     build(verbose=True)

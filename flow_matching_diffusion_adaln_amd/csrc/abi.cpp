@@ -2,9 +2,12 @@
 // the launch sequences of the block (bf16 and FP8), the two-stage stack with
 // classifier-free guidance and the flow-matching sampler.  Every check runs
 // before the first launch, so an error leaves all outputs untouched.
+#include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+
+#include <atomic>
 
 #include "dit.h"
 #include "kernels.h"
@@ -19,7 +22,7 @@ const float kQMul = (1.0f / sqrtf((float)DIT_HEAD_DIM)) * 1.4426950408889634f;
 constexpr size_t kAlign = 256;
 constexpr long long kMaxBytes = 1ll << 32;
 
-size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+constexpr size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
@@ -71,6 +74,12 @@ struct Workspace {
   size_t bytes;
 };
 
+// Bytes of the block workspace for N tokens of width D and MLP hidden F (the
+// sum of the regions `layout` places).
+constexpr size_t block_ws_bytes(size_t N, size_t D, size_t F) {
+  return 4 * round_up(N * D * 2) + round_up(N * (D + F) * 2) + round_up(dit::kGemmPartialBytes);
+}
+
 Workspace layout(const Shape& s, void* base) {
   const size_t nd = (size_t)s.N * s.D * 2;
   const size_t ncat = (size_t)s.N * (s.D + s.F) * 2;
@@ -93,11 +102,54 @@ Workspace layout(const Shape& s, void* base) {
   return w;
 }
 
+// ---- the block with a file-scope scratch (no allocation by the caller) -----
+//
+// Every GPU the library runs on holds one copy of `scratch` until the process
+// ends.  In host code the array's name is only a stand-in for the device
+// symbol: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device (with that device current) and
+// kept in `g_scratch`; only that pointer is ever handed to kernels.
+constexpr size_t kScratchBytes =
+    block_ws_bytes(DIT_NOALLOC_MAX_TOKENS, DIT_NOALLOC_WIDTH, DIT_NOALLOC_MLP_HIDDEN);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch, or null with *rc set.
+void* scratch_ptr(int* rc) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *rc = DIT_ERR_HIP;
+    return nullptr;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // two threads may both get here on first use; they store the same address
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      *rc = DIT_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_ERR_HIP; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + nb && y < x + na;
+}
+
+// Null and alignment checks of the block's tensor arguments.
+int check_block_ptrs(const void* x, const void* mod, const int32_t* pos, const void* w_in,
+                     const void* w_out, const void* q_scale, const void* k_scale, const void* y) {
+  if (!x || !mod || !pos || !w_in || !w_out || !q_scale || !k_scale || !y) return DIT_ERR_NULL;
+  if (misaligned(x) || misaligned(mod) || misaligned(pos) || misaligned(w_in) ||
+      misaligned(w_out) || misaligned(q_scale) || misaligned(k_scale) || misaligned(y))
+    return DIT_ERR_ALIGN;
+  return DIT_OK;
 }
 
 int block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const int32_t* pos,
@@ -108,12 +160,9 @@ int block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const 
   int rc = check_desc(desc, &s);
   if (rc != DIT_OK) return rc;
   if (s.N == 0) return DIT_OK;
-  if (!x || !mod || !pos || !w_in || !w_out || !q_scale || !k_scale || !y || !workspace)
-    return DIT_ERR_NULL;
-  if (misaligned(x) || misaligned(mod) || misaligned(pos) || misaligned(w_in) ||
-      misaligned(w_out) || misaligned(q_scale) || misaligned(k_scale) || misaligned(y) ||
-      misaligned(workspace))
-    return DIT_ERR_ALIGN;
+  if ((rc = check_block_ptrs(x, mod, pos, w_in, w_out, q_scale, k_scale, y)) != DIT_OK) return rc;
+  if (!workspace) return DIT_ERR_NULL;
+  if (misaligned(workspace)) return DIT_ERR_ALIGN;
   Workspace w = layout(s, workspace);
   if (ws_bytes < w.bytes) return DIT_ERR_WORKSPACE;
   if (overlaps(y, (size_t)s.N * s.D * 2, workspace, w.bytes)) return DIT_ERR_ARG;
@@ -460,6 +509,29 @@ int dit_block_fwd_events(const dit_block_desc* desc, const void* x, const void* 
   if (!events) return DIT_ERR_NULL;
   return block_fwd(desc, x, mod, pos, w_in, w_out, q_scale, k_scale, y, workspace,
                    workspace_bytes, stream, events);
+}
+
+int dit_block_fwd_noalloc(const dit_block_desc* desc, const void* x, const void* mod,
+                          const int32_t* pos, const void* w_in, const void* w_out,
+                          const void* q_scale, const void* k_scale, void* y, hipStream_t stream) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc != DIT_OK) return rc;
+  if (s.N == 0) return DIT_OK;
+  // sizes beyond the scratch, and bad pointers, are refused before anything
+  // touches the device
+  if (layout(s, nullptr).bytes > kScratchBytes) return DIT_ERR_WORKSPACE;
+  if ((rc = check_block_ptrs(x, mod, pos, w_in, w_out, q_scale, k_scale, y)) != DIT_OK) return rc;
+  void* ws = scratch_ptr(&rc);
+  if (!ws) return rc;
+  return block_fwd(desc, x, mod, pos, w_in, w_out, q_scale, k_scale, y, ws, kScratchBytes, stream,
+                   nullptr);
+}
+
+int dit_block_noalloc_scratch_bytes(size_t* bytes) {
+  if (!bytes) return DIT_ERR_NULL;
+  *bytes = kScratchBytes;
+  return DIT_OK;
 }
 
 int dit_attn_fwd(int32_t n_tokens, int32_t n_heads, int32_t head_dim, const void* q,

@@ -27,7 +27,8 @@ EXPORTS = ("dit_block_workspace_bytes", "dit_block_fwd", "dit_block_fwd_events",
            "dit_flow_sigmas", "dit_sampler_workspace_bytes", "dit_sampler_prepare",
            "dit_sampler_step", "dit_linear", "dit_time_sinusoid", "dit_quantize_rows_fp8",
            "dit_block_fp8_workspace_bytes", "dit_block_fwd_fp8", "dit_block_fwd_fp8_events",
-           "dit_status_str")
+           "dit_block_fwd_noalloc", "dit_block_noalloc_scratch_bytes", "dit_status_str")
+NOALLOC_MAX_TOKENS = 4352
 N_GROUPS = 4        # block groups with their own modulation: stage-1 image, reference, text; joint
 TIME_DIM = 256
 
@@ -129,6 +130,8 @@ def load_library() -> ctypes.CDLL:
     lib.dit_block_fwd_fp8.argtypes = [desc_p] + [vp] * 10 + [vp, sz, vp]
     lib.dit_block_fwd_fp8_events.argtypes = [desc_p] + [vp] * 10 + [vp, sz, vp,
                                                                    ctypes.POINTER(vp)]
+    lib.dit_block_fwd_noalloc.argtypes = [desc_p] + [vp] * 8 + [vp]
+    lib.dit_block_noalloc_scratch_bytes.argtypes = [ctypes.POINTER(sz)]
     lib.dit_status_str.argtypes = [ctypes.c_int]
     lib.dit_status_str.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -223,6 +226,36 @@ def block_fwd(x, mod, pos, w_in, w_out, q_scale, k_scale, desc: BlockDesc, y=Non
     else:
         arr = (ctypes.c_void_p * (N_STAGES + 1))(*events)
         _check(lib.dit_block_fwd_events(*args, arr))
+    return y
+
+
+def noalloc_scratch_bytes() -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().dit_block_noalloc_scratch_bytes(ctypes.byref(n)))
+    return n.value
+
+
+def block_fwd_noalloc(x, mod, pos, w_in, w_out, q_scale, k_scale, desc: BlockDesc, y=None,
+                      stream=None) -> torch.Tensor:
+    """y = dit_block_fwd_noalloc(...): the block with the library's own per-GPU
+    scratch instead of a workspace argument (y is allocated here when not given)."""
+    N = sum(desc.n_tokens[i] for i in range(desc.n_streams))
+    D, F, d = desc.width, desc.mlp_hidden, desc.head_dim
+    _bf16(x, (N, D), "x")
+    _bf16(mod, (desc.n_streams, 3, D), "mod")
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (N, 4) or not pos.is_cuda \
+            or not pos.is_contiguous():
+        raise ValueError("pos must be a contiguous int32 [N, 4] GPU tensor")
+    _bf16(w_in, (3 * D + 2 * F, D), "w_in")
+    _bf16(w_out, (D, D + F), "w_out")
+    _bf16(q_scale, (d,), "q_scale")
+    _bf16(k_scale, (d,), "k_scale")
+    if y is None:
+        y = torch.empty_like(x)
+    _bf16(y, (N, D), "y")
+    _check(load_library().dit_block_fwd_noalloc(
+        ctypes.byref(desc), _ptr(x), _ptr(mod), _ptr(pos), _ptr(w_in), _ptr(w_out),
+        _ptr(q_scale), _ptr(k_scale), _ptr(y), _stream(stream)))
     return y
 
 

@@ -123,6 +123,32 @@ int dit_block_fwd_events(const dit_block_desc* desc, const void* x, const void* 
                          const void* q_scale, const void* k_scale, void* y, void* workspace,
                          size_t workspace_bytes, hipStream_t stream, void* const* events);
 
+/* ---- The block without a caller-supplied workspace --------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the block
+ * of dit_block_fwd with its workspace in a file-scope device array of the
+ * library (dit_block_noalloc_scratch_bytes() bytes per GPU, about 348 MB),
+ * held from the library's first use on that GPU until the process ends.  The array is sized for the
+ * FLUX.3 block (width 3072, mlp_hidden 9216) at up to DIT_NOALLOC_MAX_TOKENS
+ * tokens (a 1024^2 image with up to 256 text tokens, or any stage-1 block of
+ * it); a descriptor whose workspace would not fit is refused with
+ * DIT_ERR_WORKSPACE before anything is launched.  Arguments, results and
+ * other errors as for dit_block_fwd; the call itself allocates nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (several streams, or several host threads) race and must be
+ * serialized by the caller.  The array keeps the last call's contents; the
+ * block writes every part of it it reads before reading it. */
+#define DIT_NOALLOC_MAX_TOKENS 4352
+#define DIT_NOALLOC_WIDTH 3072
+#define DIT_NOALLOC_MLP_HIDDEN 9216
+
+int dit_block_fwd_noalloc(const dit_block_desc* desc, const void* x, const void* mod,
+                          const int32_t* pos, const void* w_in, const void* w_out,
+                          const void* q_scale, const void* k_scale, void* y, hipStream_t stream);
+
+/* Size in bytes of that per-GPU array (host query, no device access). */
+int dit_block_noalloc_scratch_bytes(size_t* bytes);
+
 /* Full (unmasked) multi-head attention over all N tokens
  * ("How it works": full attention in the 28 joint blocks; padding attended).
  *   q, k, v  bf16 [N, H, d]   o  bf16 [N, H, d] (must not overlap q, k, v)

@@ -496,3 +496,34 @@ def test_struct_layouts_match_a_c_compiler(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(cls), cname
         for fname, _ in cls._fields_:
             assert got[(cname, fname)] == getattr(cls, fname).offset, (cname, fname)
+
+
+def test_noalloc_scratch_and_host_errors(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.dit_block_noalloc_scratch_bytes(ctypes.byref(n)) == OK
+    assert lib.dit_block_noalloc_scratch_bytes(None) == NULL
+    # the scratch holds exactly the workspace of the largest sequence it serves
+    assert ws(lib, ops.make_desc([ops.NOALLOC_MAX_TOKENS]))[1] == n.value
+    assert ws(lib, ops.make_desc([4096, 256]))[1] <= n.value
+    text = open(HEADER).read()
+    assert re.search(r"#define DIT_NOALLOC_MAX_TOKENS %d\b" % ops.NOALLOC_MAX_TOKENS, text)
+
+    def call(desc, ptrs):
+        args = [ctypes.byref(desc)] + [ctypes.c_void_p(v) if v else None for v in ptrs] + [None]
+        return lib.dit_block_fwd_noalloc(*args)
+
+    p = [P + (1 << 30) * j for j in range(8)]
+    # one token too many (or a wider block that no longer fits) is refused
+    # before the device is touched
+    assert call(ops.make_desc([ops.NOALLOC_MAX_TOKENS + 1]), p) == WS
+    assert call(ops.make_desc([4096, 257]), p) == WS
+    assert call(ops.make_desc([4096], width=4096, n_heads=32), p) == WS
+    for i in range(8):
+        q = list(p)
+        q[i] = 0
+        assert call(ops.make_desc([256, 80]), q) == NULL, i
+        q[i] = BAD + (1 << 30) * i
+        assert call(ops.make_desc([256, 80]), q) == ALIGN, i
+    # shape errors and the empty call come first, as in dit_block_fwd
+    assert call(ops.make_desc([256, 80], head_dim=64, n_heads=48), p) == UNSUP
+    assert call(ops.make_desc([0, 0]), [0] * 8) == OK

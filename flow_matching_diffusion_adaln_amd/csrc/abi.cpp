@@ -70,14 +70,20 @@ int check_desc(const dit_block_desc* d, Shape* sh) {
 
 struct Workspace {
   uint16_t *u, *q, *k, *v, *cat;
-  float* partial;  // GEMM split-K partial tiles
+  float* partial;  // GEMM split-K partial tiles; attention's split partials
+  int* attn_cnt;   // attention's split counters, zeroed by the AdaLN launch
   size_t bytes;
 };
+
+// Attention counters in the block workspace (one per cut between two CU
+// shares; more than any GPU has CUs).
+constexpr int kAttnCounters = 1024;
 
 // Bytes of the block workspace for N tokens of width D and MLP hidden F (the
 // sum of the regions `layout` places).
 constexpr size_t block_ws_bytes(size_t N, size_t D, size_t F) {
-  return 4 * round_up(N * D * 2) + round_up(N * (D + F) * 2) + round_up(dit::kGemmPartialBytes);
+  return 4 * round_up(N * D * 2) + round_up(N * (D + F) * 2) + round_up(dit::kGemmPartialBytes) +
+         round_up(kAttnCounters * sizeof(int));
 }
 
 Workspace layout(const Shape& s, void* base) {
@@ -98,8 +104,17 @@ Workspace layout(const Shape& s, void* base) {
   off += round_up(ncat);
   w.partial = reinterpret_cast<float*>(p + off);
   off += round_up(dit::kGemmPartialBytes);
+  w.attn_cnt = reinterpret_cast<int*>(p + off);
+  off += round_up(kAttnCounters * sizeof(int));
   w.bytes = off;
   return w;
+}
+
+// The attention split of a block: the GEMM partial region is free between
+// the input projection's fix-up and the output projection, and the counters
+// were zeroed by the block's AdaLN launch.
+dit::AttnSplit block_attn_split(const Workspace& w) {
+  return dit::AttnSplit{w.partial, dit::kGemmPartialBytes, w.attn_cnt, kAttnCounters, false};
 }
 
 // ---- the block with a file-scope scratch (no allocation by the caller) -----
@@ -179,7 +194,7 @@ int block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const 
   const uint16_t* mb = static_cast<const uint16_t*>(mod);
   if ((rc = mark(DIT_STAGE_ADALN))) return rc;
   if ((rc = hip_status(dit::launch_adaln(xb, mb, w.u, s.N, s.D, s.e0, s.e1, desc->ln_eps,
-                                         stream))))
+                                         stream, w.attn_cnt, kAttnCounters))))
     return rc;
   if ((rc = mark(DIT_STAGE_GEMM_IN))) return rc;
   // the input projection applies the QK RMSNorm and RoPE in its epilogue, so
@@ -191,10 +206,12 @@ int block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const 
     return rc;
   if ((rc = mark(DIT_STAGE_ROPE))) return rc;
   if ((rc = mark(DIT_STAGE_ATTN))) return rc;
+  const dit::AttnSplit split = block_attn_split(w);
   if ((rc = hip_status(dit::launch_attn(w.q, w.k, w.v, w.cat, s.N, s.H, s.D, s.D + s.F,
                                         1.0f / sqrtf((float)DIT_HEAD_DIM),
                                         static_cast<const uint16_t*>(q_scale),
-                                        static_cast<const uint16_t*>(k_scale), 1, stream))))
+                                        static_cast<const uint16_t*>(k_scale), 1, &split,
+                                        stream))))
     return rc;
   if ((rc = mark(DIT_STAGE_GEMM_OUT))) return rc;
   if ((rc = hip_status(dit::launch_gemm_out(w.cat, static_cast<const uint16_t*>(w_out), s.N,
@@ -261,7 +278,8 @@ int block_fwd_fp8(const dit_block_desc* desc, const void* x, const void* mod, co
   const uint16_t* mb = static_cast<const uint16_t*>(mod);
   if ((rc = mark(DIT_STAGE_ADALN))) return rc;
   if ((rc = hip_status(dit::launch_adaln_fp8(xb, mb, w.u8, w.u_scale, s.N, s.D, s.e0, s.e1,
-                                             desc->ln_eps, stream))))
+                                             desc->ln_eps, stream, w.base.attn_cnt,
+                                             kAttnCounters))))
     return rc;
   if ((rc = mark(DIT_STAGE_GEMM_IN))) return rc;
   if ((rc = hip_status(dit::launch_gemm_in_fp8(
@@ -272,10 +290,12 @@ int block_fwd_fp8(const dit_block_desc* desc, const void* x, const void* mod, co
     return rc;
   if ((rc = mark(DIT_STAGE_ROPE))) return rc;
   if ((rc = mark(DIT_STAGE_ATTN))) return rc;
+  const dit::AttnSplit split = block_attn_split(b);
   if ((rc = hip_status(dit::launch_attn(b.q, b.k, b.v, b.cat, s.N, s.H, s.D, s.D + s.F,
                                         1.0f / sqrtf((float)DIT_HEAD_DIM),
                                         static_cast<const uint16_t*>(q_scale),
-                                        static_cast<const uint16_t*>(k_scale), 1, stream))))
+                                        static_cast<const uint16_t*>(k_scale), 1, &split,
+                                        stream))))
     return rc;
   if ((rc = mark(DIT_STAGE_GEMM_OUT))) return rc;
   // the output projection's input [o | m] is quantized rowwise first
@@ -482,6 +502,55 @@ int dcopy(void* dst, const void* src, size_t n, hipStream_t stream) {
   return hip_status(hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, stream));
 }
 
+// ---- attention on its own -----------------------------------------------
+
+int check_attn(int32_t n_tokens, int32_t n_heads, int32_t head_dim, float softmax_scale) {
+  if (n_tokens < 0 || n_tokens > DIT_MAX_TOKENS || n_heads <= 0 || head_dim <= 0)
+    return DIT_ERR_SHAPE;
+  if (head_dim != DIT_HEAD_DIM) return DIT_ERR_UNSUPPORTED;
+  if ((long long)n_heads * head_dim > 65536) return DIT_ERR_UNSUPPORTED;
+  if ((long long)n_tokens * n_heads * head_dim * 2 >= kMaxBytes) return DIT_ERR_UNSUPPORTED;
+  if (bad_float(softmax_scale, true)) return DIT_ERR_ARG;
+  return DIT_OK;
+}
+
+// Workspace of dit_attn_fwd_ws: the split partials for up to kAttnMaxShares
+// shares (one per CU), then their counters.
+constexpr int kAttnMaxShares = 256;
+const size_t kAttnPartBytes = dit::attn_split_bytes(kAttnMaxShares);
+const size_t kAttnWsBytes = round_up(kAttnPartBytes) + round_up(kAttnMaxShares * sizeof(int));
+
+int attn_fwd(int32_t n_tokens, int32_t n_heads, int32_t head_dim, const void* q, const void* k,
+             const void* v, void* o, float softmax_scale, void* workspace, size_t ws_bytes,
+             bool use_ws, hipStream_t stream) {
+  int rc = check_attn(n_tokens, n_heads, head_dim, softmax_scale);
+  if (rc != DIT_OK) return rc;
+  if (n_tokens == 0) return DIT_OK;
+  if (!q || !k || !v || !o || (use_ws && !workspace)) return DIT_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) ||
+      (use_ws && misaligned(workspace)))
+    return DIT_ERR_ALIGN;
+  if (use_ws && ws_bytes < kAttnWsBytes) return DIT_ERR_WORKSPACE;
+  const size_t bytes = (size_t)n_tokens * n_heads * head_dim * 2;
+  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
+    return DIT_ERR_ARG;
+  if (use_ws && (overlaps(workspace, kAttnWsBytes, o, bytes) ||
+                 overlaps(workspace, kAttnWsBytes, q, bytes) ||
+                 overlaps(workspace, kAttnWsBytes, k, bytes) ||
+                 overlaps(workspace, kAttnWsBytes, v, bytes)))
+    return DIT_ERR_ARG;
+  const int ld = n_heads * head_dim;
+  char* wsp = static_cast<char*>(workspace);
+  const dit::AttnSplit split{wsp, kAttnPartBytes,
+                             reinterpret_cast<int*>(wsp + round_up(kAttnPartBytes)),
+                             kAttnMaxShares, true};
+  return hip_status(dit::launch_attn(static_cast<const uint16_t*>(q),
+                                     static_cast<const uint16_t*>(k),
+                                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
+                                     n_tokens, n_heads, ld, ld, softmax_scale, nullptr, nullptr,
+                                     0, use_ws ? &split : nullptr, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -536,24 +605,24 @@ int dit_block_noalloc_scratch_bytes(size_t* bytes) {
 
 int dit_attn_fwd(int32_t n_tokens, int32_t n_heads, int32_t head_dim, const void* q,
                  const void* k, const void* v, void* o, float softmax_scale, hipStream_t stream) {
-  if (n_tokens < 0 || n_tokens > DIT_MAX_TOKENS || n_heads <= 0 || head_dim <= 0)
-    return DIT_ERR_SHAPE;
-  if (head_dim != DIT_HEAD_DIM) return DIT_ERR_UNSUPPORTED;
-  if ((long long)n_heads * head_dim > 65536) return DIT_ERR_UNSUPPORTED;
-  if ((long long)n_tokens * n_heads * head_dim * 2 >= kMaxBytes) return DIT_ERR_UNSUPPORTED;
-  if (bad_float(softmax_scale, true)) return DIT_ERR_ARG;
-  if (n_tokens == 0) return DIT_OK;
-  if (!q || !k || !v || !o) return DIT_ERR_NULL;
-  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o)) return DIT_ERR_ALIGN;
-  const size_t bytes = (size_t)n_tokens * n_heads * head_dim * 2;
-  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
-    return DIT_ERR_ARG;
-  const int ld = n_heads * head_dim;
-  return hip_status(dit::launch_attn(static_cast<const uint16_t*>(q),
-                                     static_cast<const uint16_t*>(k),
-                                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
-                                     n_tokens, n_heads, ld, ld, softmax_scale, nullptr,
-                                     nullptr, 0, stream));
+  return attn_fwd(n_tokens, n_heads, head_dim, q, k, v, o, softmax_scale, nullptr, 0, false,
+                  stream);
+}
+
+int dit_attn_workspace_bytes(int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                             size_t* bytes) {
+  const int rc = check_attn(n_tokens, n_heads, head_dim, 1.0f);
+  if (rc != DIT_OK) return rc;
+  if (!bytes) return DIT_ERR_NULL;
+  *bytes = kAttnWsBytes;
+  return DIT_OK;
+}
+
+int dit_attn_fwd_ws(int32_t n_tokens, int32_t n_heads, int32_t head_dim, const void* q,
+                    const void* k, const void* v, void* o, float softmax_scale, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  return attn_fwd(n_tokens, n_heads, head_dim, q, k, v, o, softmax_scale, workspace,
+                  workspace_bytes, true, stream);
 }
 
 int rope4_apply(int32_t n_tokens, int32_t n_heads, int32_t head_dim, void* q, void* k,

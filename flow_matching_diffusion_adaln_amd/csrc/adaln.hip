@@ -25,8 +25,11 @@ __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t* __restrict__
                                                     uint16_t* __restrict__ out,
                                                     uint8_t* __restrict__ q8,
                                                     float* __restrict__ q_scale, int n_rows,
-                                                    int e0, int e1, float eps) {
+                                                    int e0, int e1, float eps,
+                                                    int* __restrict__ clear, int n_clear) {
   constexpr int W = 512 * CPL;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n_clear; i += 256) clear[i] = 0;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n_rows) return;
@@ -113,13 +116,13 @@ namespace {
 template <bool F8>
 hipError_t adaln_launch(const uint16_t* x, const uint16_t* mod, uint16_t* out, uint8_t* q8,
                         float* q_scale, int n_rows, int width, int e0, int e1, float eps,
-                        hipStream_t stream) {
+                        hipStream_t stream, int* clear, int n_clear) {
   const dim3 grid((n_rows + 3) / 4), block(256);
   switch (width / 512) {
 #define DIT_ADALN_CASE(C)                                                                        \
   case C:                                                                                        \
     hipLaunchKernelGGL((adaln_kernel<C, F8>), grid, block, 0, stream, x, mod, out, q8, q_scale,  \
-                       n_rows, e0, e1, eps);                                                     \
+                       n_rows, e0, e1, eps, clear, n_clear);                                     \
     break;
     DIT_ADALN_CASE(1) DIT_ADALN_CASE(2) DIT_ADALN_CASE(3) DIT_ADALN_CASE(4)
     DIT_ADALN_CASE(5) DIT_ADALN_CASE(6) DIT_ADALN_CASE(7) DIT_ADALN_CASE(8)
@@ -135,14 +138,17 @@ hipError_t adaln_launch(const uint16_t* x, const uint16_t* mod, uint16_t* out, u
 }  // namespace
 
 hipError_t launch_adaln(const uint16_t* x, const uint16_t* mod, uint16_t* out, int n_rows,
-                        int width, int e0, int e1, float eps, hipStream_t stream) {
-  return adaln_launch<false>(x, mod, out, nullptr, nullptr, n_rows, width, e0, e1, eps, stream);
+                        int width, int e0, int e1, float eps, hipStream_t stream, int* clear,
+                        int n_clear) {
+  return adaln_launch<false>(x, mod, out, nullptr, nullptr, n_rows, width, e0, e1, eps, stream,
+                             clear, n_clear);
 }
 
 hipError_t launch_adaln_fp8(const uint16_t* x, const uint16_t* mod, uint8_t* q8, float* q_scale,
                             int n_rows, int width, int e0, int e1, float eps,
-                            hipStream_t stream) {
-  return adaln_launch<true>(x, mod, nullptr, q8, q_scale, n_rows, width, e0, e1, eps, stream);
+                            hipStream_t stream, int* clear, int n_clear) {
+  return adaln_launch<true>(x, mod, nullptr, q8, q_scale, n_rows, width, e0, e1, eps, stream,
+                            clear, n_clear);
 }
 
 }  // namespace dit

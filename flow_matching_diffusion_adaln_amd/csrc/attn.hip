@@ -38,8 +38,24 @@
 //    checks and the FMA before each exp drop out of the loop.  Each tile's
 //    softmax is then split in halves over both MFMA steps (see run_fixed).
 //    Together about 20% of the kernel's time at 4,256 tokens.
-//  * Workgroups of one head are kept on one XCD so its K and V stay in that
-//    XCD's L2.
+//  * Work split.  The work is the grid of (head, 256-query tile, 64-key
+//    tile) iterations, heads outermost.  When there are more (head, query
+//    tile) items than CUs, one workgroup per CU takes an equal contiguous
+//    share of the iterations, so no last round of whole items leaves CUs
+//    idle (at 4,256 tokens the 408 items are 1.59 rounds of 256 CUs).  A
+//    share can end part-way through an item; since every share is at least
+//    one item long, an item is cut at most once, between two neighbouring
+//    workgroups.  Each part stores its unnormalized output, row sums and row
+//    max (fp32) to a scratch slot of the workspace and counts itself in on
+//    the slot's counter; whichever part arrives second reads the other's
+//    partial, merges it (the two parts' weights share no reference, so the
+//    merge rescales by exp2 of their max differences; with the fixed
+//    reference below it is a plain sum) and stores o.  No workgroup ever
+//    waits for another, and the merge is symmetric in the two parts, so the
+//    result does not depend on which arrives first.  With at most as many
+//    items as CUs (or no scratch) each workgroup runs one whole item.
+//  * Shares of neighbouring workgroups sit on one XCD (and so do the items of
+//    one head), so K and V and the split partials stay in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -96,45 +112,56 @@ __device__ __forceinline__ void barrier_keep_loads() {
   asm volatile("" ::: "memory");
 }
 
+// Split partials: a part is NWAVE waves x PGROUPS 16-byte groups x 64 lanes
+// (a lane's 64 accumulators, then its row sum l and row max m), group-major
+// per wave so each wave store or load moves 1 KB contiguously.  Slot s (the
+// boundary between shares s - 1 and s) holds the two parts of the item cut
+// there: part 0 the keys before the cut, part 1 the keys after it.
+constexpr int PGROUPS = 17;
+// cache-policy bits of the buffer loads and stores: device scope (sc1)
+constexpr int kScopeDevice = 16;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 }  // namespace
 
-__global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t* __restrict__ q,
-                                                          const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v,
-                                                          uint16_t* __restrict__ o, int N,
-                                                          int H, int ld_qkv, int ld_o,
-                                                          float c, float c_bound,
-                                                          const uint16_t* __restrict__ q_scale,
-                                                          const uint16_t* __restrict__ k_scale,
-                                                          int prescaled) {
+__global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, int N, int H, int ld_qkv,
+    int ld_o, float c, float c_bound, const uint16_t* __restrict__ q_scale,
+    const uint16_t* __restrict__ k_scale, int prescaled, void* __restrict__ part,
+    int part_bytes, int* __restrict__ cnt) {
   // distinct arrays per stage: reads of one stage never wait on the
   // direct-to-LDS loads in flight into the other
   __shared__ __attribute__((aligned(16))) uint16_t s_k0[BKEY * HD];
   __shared__ __attribute__((aligned(16))) uint16_t s_v0[BKEY * HD];
   __shared__ __attribute__((aligned(16))) uint16_t s_k1[BKEY * HD];
   __shared__ __attribute__((aligned(16))) uint16_t s_v1[BKEY * HD];
+  __shared__ int s_arrival;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, hl = lane >> 5;
   const int nqt = (N + BQ - 1) / BQ;
-  const int id = xcd_remap(blockIdx.x, nqt * H);
-  const int h = id / nqt, qt = id % nqt;
-  const int q0 = qt * BQ + wave * 32;
+  const int ntiles = (N + BKEY - 1) / BKEY;
+  // This workgroup's share [b0, b1) of the nqt * H * ntiles iterations
+  // (item = head * nqt + query tile, then key tile).  With one share per item
+  // (gridDim.x == nqt * H) every share is exactly one whole item.
+  const int G = gridDim.x;
+  const int r = xcd_remap(blockIdx.x, G);
+  const long long total = (long long)nqt * H * ntiles;
+  const long long b0 = total * r / G, b1 = total * (r + 1) / G;
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds q[q0 + ln][16 s + 8 hl .. + 8]
+  // Per-segment state read by the loops below: the head's K and V, the first
+  // key tile kt0 and tile count nt of the segment, and the number of keys
+  // that count in its last tile (lim_seg < 64 only in the last tile of a
+  // ragged N).
+  const char* kbase;
+  const char* vbase;
+  int kt0 = 0, nt = 0, lim_seg = BKEY;
   bf16x8 qf[8];
-  {
-    const int qi = min(q0 + ln, N - 1);
-    const uint4* qp = reinterpret_cast<const uint4*>(q + (size_t)qi * ld_qkv + (size_t)h * HD);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, qp[2 * s + hl]);
-  }
 
   // Direct-to-LDS loads: a wave instruction fills 1 KB = 4 rows of 256 B;
   // lane i lands in row 4 j' + i / 16 at physical chunk i % 16.  Wave w
   // fills rows [4 LPW w, 4 LPW (w + 1)) of a tile.
-  const char* kbase = reinterpret_cast<const char*>(k + (size_t)h * HD);
-  const char* vbase = reinterpret_cast<const char*>(v + (size_t)h * HD);
   const int prow = lane >> 4, pch = lane & 15;
   // byte offsets of the chunk this lane fetches for slab j (recomputed per
   // load: a few integer ops instead of 8 live registers)
@@ -145,13 +172,14 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
     return (uint32_t)(((((pch >> 2) ^ vswz(wave * 4 * LPW + 4 * j + prow)) << 2) | (pch & 3)) * 16);
   };
   const uint32_t row_bytes = (uint32_t)ld_qkv * 2u;
-  const int ntiles = (N + BKEY - 1) / BKEY;
-  // tiles past the end reload the last one into an idle slot (never read)
+  // tile t of the segment (key tile kt0 + t); tiles past the end of the
+  // sequence reload the last one into an idle slot (never read), tiles past
+  // the segment's end load real keys that are never read either
   auto dma_k = [&](int t, uint16_t* sk) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      const int r = wave * 4 * LPW + 4 * j + prow;
-      const uint32_t key = (uint32_t)min(min(t, ntiles - 1) * BKEY + r, N - 1);
+      const int rw = wave * 4 * LPW + 4 * j + prow;
+      const uint32_t key = (uint32_t)min(min(kt0 + t, ntiles - 1) * BKEY + rw, N - 1);
       __builtin_amdgcn_global_load_lds(kbase + (key * row_bytes + kch(j)),
                                        (lds_ptr)(sk + (wave * 4 * LPW + 4 * j) * HD), 16, 0, 0);
     }
@@ -159,8 +187,8 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
   auto dma_v = [&](int t, uint16_t* sv) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      const int r = wave * 4 * LPW + 4 * j + prow;
-      const uint32_t key = (uint32_t)min(min(t, ntiles - 1) * BKEY + r, N - 1);
+      const int rw = wave * 4 * LPW + 4 * j + prow;
+      const uint32_t key = (uint32_t)min(min(kt0 + t, ntiles - 1) * BKEY + rw, N - 1);
       __builtin_amdgcn_global_load_lds(vbase + (key * row_bytes + vch(j)),
                                        (lds_ptr)(sv + (wave * 4 * LPW + 4 * j) * HD), 16, 0, 0);
     }
@@ -182,12 +210,8 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
     voff[d] = vrow * 256 + ((d ^ vswz(vrow)) << 6) + (16 * (g & 1) + 4 * (gi & 3)) * 2;
 
   f32x16 acc[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
-  float m_run = -INFINITY;  // running max, already multiplied by c
-  float l_run = 0.f;
+  float m_run;  // running max, already multiplied by c
+  float l_run;
 
   // Fixed reference.  When q and k come out of the block's QK RMSNorm with
   // scales g_q, g_k, every row has |q| <= sqrt(128) max|g_q| (and likewise
@@ -211,7 +235,9 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
       gk = fmaxf(gk, __shfl_xor(gk, off, 64));
     }
     const float bound = c_bound * 128.0f * gq * gk * 1.01f;
-    fixed = bound <= 40.0f;  // false for NaN: the running max then
+    // uniform over the workgroup (a wave-wide max); read as a scalar so the
+    // branch on it is a scalar branch
+    fixed = __builtin_amdgcn_readfirstlane(bound <= 40.0f ? 1 : 0) != 0;  // NaN: running max
   }
 
   // S^T = K Q^T for one key tile: 2 key blocks of 32, 8 k steps of 16 dims.
@@ -227,7 +253,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+      for (int rr = 0; rr < 16; ++rr) sc[kb][rr] = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i + 1 < 16) fk[(i + 1) & 1] = kfrag(skb, i + 1);
@@ -242,7 +268,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sc[kb][rr]);
     return fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
   };
   auto rescale = [&](float mx) __attribute__((always_inline)) {
@@ -254,7 +280,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+        for (int rr = 0; rr < 16; ++rr) acc[d][rr] *= alpha;
     }
   };
   // P = exp2(S c - m) in bf16 for the PV MFMA; with `lim` < 64 keys at local
@@ -262,14 +288,17 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
   auto softmax = [&](const f32x16 (&sc)[2], bf16x8 (&pb)[4], int lim)
       __attribute__((always_inline)) {
     float psum = 0.f;
+    // key index 32 kb + 16 (rr / 8) + 8 hl + rr % 8 against lim, with the
+    // lane's part moved to the bound (no per-lane index constants)
+    const int lim_l = lim - 8 * hl;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, -m_run));
-        if (lim < BKEY && 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7) >= lim) p = 0.f;
+      for (int rr = 0; rr < 16; ++rr) {
+        float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][rr], c, -m_run));
+        if (lim < BKEY && 32 * kb + 16 * (rr >> 3) + (rr & 7) >= lim_l) p = 0.f;
         psum += p;
-        pb[2 * kb + (r >> 3)][r & 7] = (__bf16)p;
+        pb[2 * kb + (rr >> 3)][rr & 7] = (__bf16)p;
       }
     l_run += psum;
   };
@@ -293,7 +322,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
     }
   };
 
-  // the key loop with the running max
+  // the key loop of one segment with the running max
   auto run_online = [&]() __attribute__((always_inline)) {
     // Software pipeline over key tiles.  Iteration t holds S(t) and its row
     // max; it computes S(t + 1) = K(t + 1) Q^T while the softmax of S(t) runs
@@ -360,15 +389,15 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
     auto last = [&](auto slot, f32x16 (&cur)[2], float mx_cur) __attribute__((always_inline)) {
       constexpr int sl = decltype(slot)::value;
       rescale(mx_cur);
-      softmax(cur, pb, N - (ntiles - 1) * BKEY);
+      softmax(cur, pb, lim_seg);
       pv(ring_v[sl], pb);
     };
     int t = 0;
-    for (; t + 2 < ntiles; t += 2) {
+    for (; t + 2 < nt; t += 2) {
       iter(std::integral_constant<int, 0>{}, t, sa, mx_a, sb, mx_b);
       iter(std::integral_constant<int, 1>{}, t + 1, sb, mx_b, sa, mx_a);
     }
-    if (t + 1 < ntiles) {
+    if (t + 1 < nt) {
       iter(std::integral_constant<int, 0>{}, t, sa, mx_a, sb, mx_b);
       last(std::integral_constant<int, 1>{}, sb, mx_b);
     } else {
@@ -386,18 +415,19 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
   auto run_fixed = [&]() __attribute__((always_inline)) {
     uint16_t* const ring_k[2] = {s_k0, s_k1};
     uint16_t* const ring_v[2] = {s_v0, s_v1};
-    const int lim = N - (ntiles - 1) * BKEY;
+    const int lim = lim_seg;
     // weights of one 32-key half (kb) of a tile into its two B fragments;
     // keys at tile index >= lim get none.  Returns the half's row sum.
     auto half = [&](const f32x16& sv, int kb, bf16x8 (&ph)[2], int lm)
         __attribute__((always_inline)) {
       float sum = 0.f;
+      const int lm_l = lm - 8 * hl;  // the lane's part of the key index moved to the bound
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(sv[r]);
-        if (lm < BKEY && 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7) >= lm) p = 0.f;
+      for (int rr = 0; rr < 16; ++rr) {
+        float p = __builtin_amdgcn_exp2f(sv[rr]);
+        if (lm < BKEY && 32 * kb + 16 * (rr >> 3) + (rr & 7) >= lm_l) p = 0.f;
         sum += p;
-        ph[r >> 3][r & 7] = (__bf16)p;
+        ph[rr >> 3][rr & 7] = (__bf16)p;
       }
       return sum;
     };
@@ -422,7 +452,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
     __builtin_amdgcn_s_waitcnt(vmcnt_imm_lpw());
     barrier_keep_loads();
     qk(s_k0, sa);
-    l_run = half(sa[0], 0, pa0, ntiles == 1 ? lim : BKEY);
+    l_run = half(sa[0], 0, pa0, nt == 1 ? lim : BKEY);
     dma_v(1, s_v1);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm_lpw());
     barrier_keep_loads();
@@ -471,52 +501,183 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(const uint16_t*
     using NoMask = std::false_type;
     using Mask = std::true_type;
     int t = 0;
-    for (; t + 3 < ntiles; t += 2) {
+    for (; t + 3 < nt; t += 2) {
       iter(S0{}, NoMask{}, t, sa, sb, pa0, pb0);
       iter(S1{}, NoMask{}, t + 1, sb, sa, pb0, pa0);
     }
-    if (t + 3 == ntiles) {
+    if (t + 3 == nt) {
       iter(S0{}, NoMask{}, t, sa, sb, pa0, pb0);
       iter(S1{}, Mask{}, t + 1, sb, sa, pb0, pa0);
       last(S0{}, sa, pa0);
-    } else if (t + 2 == ntiles) {
+    } else if (t + 2 == nt) {
       iter(S0{}, Mask{}, t, sa, sb, pa0, pb0);
       last(S1{}, sb, pb0);
     } else {
       last(S0{}, sa, pa0);
     }
   };
-  if (fixed)
-    run_fixed();
-  else
-    run_online();
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm0());
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l_tot;
-  const int qi = q0 + ln;
-  if (qi < N) {
-    uint16_t* op = o + (size_t)qi * ld_o + (size_t)h * HD;
+  // The share, one segment (an item or the part of one inside the share) at
+  // a time.
+  for (long long at = b0; at < b1;) {
+    const long long seg_start = at;
+    const int item = (int)(at / ntiles);
+    const int k0 = (int)(at - (long long)item * ntiles);
+    const int k1 = (int)min((long long)ntiles, b1 - (long long)item * ntiles);
+    at = (long long)item * ntiles + k1;
+    const int h = item / nqt, qt = item % nqt;
+    const int q0 = qt * BQ + wave * 32;
+    // every wave is done with the previous segment's LDS tiles before the
+    // rings are refilled
+    if (seg_start != b0) __syncthreads();
+    kbase = reinterpret_cast<const char*>(k + (size_t)h * HD);
+    vbase = reinterpret_cast<const char*>(v + (size_t)h * HD);
+    kt0 = k0;
+    nt = k1 - k0;
+    lim_seg = k1 == ntiles ? N - (ntiles - 1) * BKEY : BKEY;
+
+    // Q fragments (B operand of S^T = K Q^T): lane holds q[q0 + ln][16 s + 8 hl .. + 8]
+    {
+      const int qi = min(q0 + ln, N - 1);
+      const uint4* qp = reinterpret_cast<const uint4*>(q + (size_t)qi * ld_qkv + (size_t)h * HD);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, qp[2 * s + hl]);
+    }
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int dim = 32 * d + 8 * r + 4 * hl;
-        const uint32_t lo = pack2(acc[d][4 * r] * inv, acc[d][4 * r + 1] * inv);
-        const uint32_t hi = pack2(acc[d][4 * r + 2] * inv, acc[d][4 * r + 3] * inv);
-        *reinterpret_cast<uint2*>(op + dim) = make_uint2(lo, hi);
+      for (int rr = 0; rr < 16; ++rr) acc[d][rr] = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
+
+    if (fixed)
+      run_fixed();
+    else
+      run_online();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm0());
+
+    if (k0 != 0 || k1 != ntiles) {
+      // A part of a cut item: store it, count it in, and if the other part is
+      // already in, merge it and finish the item here.
+      const int slot = k0 != 0 ? r : r + 1;
+      const int half_id = k0 != 0 ? 1 : 0;
+      // The partials and the counter are accessed with device-scope
+      // (coherent across the XCDs' L2s) loads, stores and atomics, so no
+      // cache-wide write-back or invalidation is needed: this part's stores
+      // are complete (vmcnt(0)) in every wave before the count is taken, and
+      // the other part's stores were complete before its count.  The 16-byte
+      // buffer forms carry the device-scope bit (the 4-byte atomic forms
+      // would take four times the store instructions).
+      const __amdgpu_buffer_rsrc_t rsrc =
+          __builtin_amdgcn_make_buffer_rsrc(part, 0, part_bytes, 0x00020000);
+      auto group_off = [&](int hid, int gi) __attribute__((always_inline)) {
+        return (int)(((((2 * slot + hid) * NWAVE + wave) * PGROUPS + gi) * 64 + lane) * 16);
+      };
+      auto st16 = [&](int gi, float a0, float a1, float a2, float a3)
+          __attribute__((always_inline)) {
+        const f32x4 w = {a0, a1, a2, a3};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, w), rsrc,
+                                               group_off(half_id, gi), 0, kScopeDevice);
+      };
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+          st16(4 * d + gq, acc[d][4 * gq], acc[d][4 * gq + 1], acc[d][4 * gq + 2],
+               acc[d][4 * gq + 3]);
+      st16(16, l_run, m_run, 0.f, 0.f);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm0());
+      __syncthreads();
+      if (tid == 0)
+        s_arrival = __hip_atomic_fetch_add(&cnt[slot], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      // first in: the other part finishes the item
+      if (__builtin_amdgcn_readfirstlane(s_arrival) == 0) continue;
+      if (tid == 0)  // ready for the next launch
+        __hip_atomic_store(&cnt[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      auto ld16 = [&](int gi) __attribute__((always_inline)) {
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rsrc, group_off(half_id ^ 1, gi), 0, kScopeDevice));
+      };
+      const f32x4 lm = ld16(16);
+      float sa = 1.f, sb = 1.f;
+      if (!fixed) {
+        // both parts' weights relative to the larger of their references;
+        // the same expression for either order of arrival
+        const float mm = fmaxf(m_run, lm[1]);
+        sa = __builtin_amdgcn_exp2f(m_run - mm);
+        sb = __builtin_amdgcn_exp2f(lm[1] - mm);
       }
+      l_run = l_run * sa + lm[0] * sb;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x4 w = ld16(4 * d + gq);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[d][4 * gq + e] = acc[d][4 * gq + e] * sa + w[e] * sb;
+        }
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = 1.0f / l_tot;
+    const int qi = q0 + ln;
+    if (qi < N) {
+      uint16_t* op = o + (size_t)qi * ld_o + (size_t)h * HD;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int dim = 32 * d + 8 * rr + 4 * hl;
+          const uint32_t lo = pack2(acc[d][4 * rr] * inv, acc[d][4 * rr + 1] * inv);
+          const uint32_t hi = pack2(acc[d][4 * rr + 2] * inv, acc[d][4 * rr + 3] * inv);
+          *reinterpret_cast<uint2*>(op + dim) = make_uint2(lo, hi);
+        }
+    }
   }
+}
+
+__global__ void attn_clear_kernel(int* __restrict__ cnt, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    cnt[i] = 0;
+}
+
+size_t attn_split_bytes(int n_slots) {
+  return (size_t)n_slots * 2 * NWAVE * PGROUPS * 64 * sizeof(float4);
 }
 
 hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                        int N, int H, int ld_qkv, int ld_o, float softmax_scale,
                        const uint16_t* q_scale, const uint16_t* k_scale, int q_prescaled,
-                       hipStream_t stream) {
+                       const AttnSplit* split, hipStream_t stream) {
   const int nqt = (N + BQ - 1) / BQ;
+  const int items = nqt * H;
+  int grid = items;
+  void* part = nullptr;
+  int part_bytes = 0;
+  int* cnt = nullptr;
+  if (split != nullptr) {
+    // one share per CU, as many as the scratch has slots for
+    int cap = device_cus();
+    while (cap > 1 && (attn_split_bytes(cap) > split->part_bytes || cap > split->n_counters))
+      --cap;
+    if (items > cap && cap > 1) {
+      grid = cap;
+      part = split->part;
+      part_bytes = (int)attn_split_bytes(grid);
+      cnt = split->counters;
+      if (split->clear) {
+        hipLaunchKernelGGL(attn_clear_kernel, dim3(1), dim3(256), 0, stream, cnt, grid);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+    }
+  }
   const float c = softmax_scale * DIT_LOG2E;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(nqt * H), dim3(64 * NWAVE), 0, stream, q, k, v, o, N, H,
-                     ld_qkv, ld_o, q_prescaled ? 1.0f : c, c, q_scale, k_scale, q_prescaled);
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(grid), dim3(64 * NWAVE), 0, stream, q, k, v, o, N, H,
+                     ld_qkv, ld_o, q_prescaled ? 1.0f : c, c, q_scale, k_scale, q_prescaled,
+                     part, part_bytes, cnt);
   return hipGetLastError();
 }
 

@@ -963,6 +963,8 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
   epilogue_pair<EPI, BM>(g, tm, tn, wm, wn, lane, i, jp, rr, a, b);
 }
 
+}  // namespace
+
 // Compute units of the current device (queried once per device).
 int device_cus() {
   // several host threads may fill an entry at once; they store the same value
@@ -977,6 +979,8 @@ int device_cus() {
   }
   return n;
 }
+
+namespace {
 
 // Work plan of one GEMM launch.  With one workgroup per CU at a time, tiles
 // run in rounds of `cus`.  A last round holding only a few tiles would leave

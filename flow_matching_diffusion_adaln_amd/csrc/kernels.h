@@ -13,14 +13,20 @@ namespace dit {
 #define GEMM_MAX_SPLIT_PIECES 256
 constexpr size_t kGemmPartialBytes = (size_t)2 * GEMM_MAX_SPLIT_PIECES * 256 * 256 * 4;
 
+// Compute units of the current device (queried once per device).
+int device_cus();
+
+// `clear` (may be null): n_clear ints the kernel sets to zero on the way
+// (the attention split counters of the same block).
 hipError_t launch_adaln(const uint16_t* x, const uint16_t* mod, uint16_t* out, int n_rows,
-                        int width, int e0, int e1, float eps, hipStream_t stream);
+                        int width, int e0, int e1, float eps, hipStream_t stream,
+                        int* clear = nullptr, int n_clear = 0);
 
 // FP8 variant: u rounded to bf16, then quantized rowwise to e4m3 codes q8
 // [n_rows, width] with one float scale per row (u ~ q8 * q_scale).
 hipError_t launch_adaln_fp8(const uint16_t* x, const uint16_t* mod, uint8_t* q8, float* q_scale,
                             int n_rows, int width, int e0, int e1, float eps,
-                            hipStream_t stream);
+                            hipStream_t stream, int* clear = nullptr, int n_clear = 0);
 
 // Rowwise e4m3 quantization of bf16 x [M, K] (K a multiple of 8): codes q
 // [M, K], scales [M] with x ~ q * scale.
@@ -33,6 +39,21 @@ hipError_t launch_rope4(uint16_t* q, uint16_t* k, const int32_t* pos, const uint
                         const uint16_t* k_scale, int n_tokens, int n_heads, float theta,
                         float eps, float q_mul, hipStream_t stream);
 
+// Scratch that lets attention cut its work into one equal share per CU:
+// `part` holds the fp32 partials of the items cut between two shares (one
+// slot per cut, attn_split_bytes(slots) bytes for `slots` slots), `counters`
+// one int per slot, all zero when the launch starts (with `clear` the launch
+// zeroes them first, otherwise the caller has).  Without it (null) every
+// workgroup runs one whole (head, 256-query) item.
+struct AttnSplit {
+  void* part;
+  size_t part_bytes;
+  int* counters;
+  int n_counters;
+  bool clear;
+};
+size_t attn_split_bytes(int n_slots);
+
 // q_scale / k_scale (both or neither): the QK RMSNorm scales q and k were
 // normalized with.  q_prescaled: q already carries softmax_scale * log2 e.
 // With both, the scores are bounded and the kernel may use a fixed softmax
@@ -40,7 +61,7 @@ hipError_t launch_rope4(uint16_t* q, uint16_t* k, const int32_t* pos, const uint
 hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                        int N, int H, int ld_qkv, int ld_o, float softmax_scale,
                        const uint16_t* q_scale, const uint16_t* k_scale, int q_prescaled,
-                       hipStream_t stream);
+                       const AttnSplit* split, hipStream_t stream);
 
 // q_mul multiplies the normalized, rotated q before it is stored
 hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D, int F,

@@ -27,7 +27,8 @@ EXPORTS = ("dit_block_workspace_bytes", "dit_block_fwd", "dit_block_fwd_events",
            "dit_flow_sigmas", "dit_sampler_workspace_bytes", "dit_sampler_prepare",
            "dit_sampler_step", "dit_linear", "dit_time_sinusoid", "dit_quantize_rows_fp8",
            "dit_block_fp8_workspace_bytes", "dit_block_fwd_fp8", "dit_block_fwd_fp8_events",
-           "dit_block_fwd_noalloc", "dit_block_noalloc_scratch_bytes", "dit_status_str")
+           "dit_block_fwd_noalloc", "dit_block_noalloc_scratch_bytes", "dit_attn_workspace_bytes",
+           "dit_attn_fwd_ws", "dit_status_str")
 NOALLOC_MAX_TOKENS = 4352
 N_GROUPS = 4        # block groups with their own modulation: stage-1 image, reference, text; joint
 TIME_DIM = 256
@@ -132,6 +133,8 @@ def load_library() -> ctypes.CDLL:
                                                                    ctypes.POINTER(vp)]
     lib.dit_block_fwd_noalloc.argtypes = [desc_p] + [vp] * 8 + [vp]
     lib.dit_block_noalloc_scratch_bytes.argtypes = [ctypes.POINTER(sz)]
+    lib.dit_attn_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+    lib.dit_attn_fwd_ws.argtypes = [i32, i32, i32, vp, vp, vp, vp, f32, vp, sz, vp]
     lib.dit_status_str.argtypes = [ctypes.c_int]
     lib.dit_status_str.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -270,6 +273,31 @@ def attn_fwd(q, k, v, o=None, softmax_scale: Optional[float] = None, stream=None
     scale = d ** -0.5 if softmax_scale is None else softmax_scale
     _check(load_library().dit_attn_fwd(N, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                        ctypes.c_float(scale), _stream(stream)))
+    return o
+
+
+def attn_workspace_bytes(n_tokens: int, n_heads: int, head_dim: int = configs.HEAD_DIM) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().dit_attn_workspace_bytes(n_tokens, n_heads, head_dim, ctypes.byref(n)))
+    return n.value
+
+
+def attn_fwd_ws(q, k, v, o=None, softmax_scale: Optional[float] = None, workspace=None,
+                stream=None):
+    """o = dit_attn_fwd_ws(q, k, v): attention with the work split over the CUs
+    (the block's schedule); q, k, v, o bf16 [N, H, d]."""
+    N, H, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _bf16(t, (N, H, d), n)
+    if o is None:
+        o = torch.empty_like(q)
+    _bf16(o, (N, H, d), "o")
+    if workspace is None:
+        workspace = torch.empty(attn_workspace_bytes(N, H, d), dtype=torch.uint8, device=q.device)
+    scale = d ** -0.5 if softmax_scale is None else softmax_scale
+    _check(load_library().dit_attn_fwd_ws(
+        N, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), ctypes.c_float(scale), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream)))
     return o
 
 

@@ -95,7 +95,17 @@ typedef struct dit_block_desc {
 
 /* Bytes of device workspace dit_block_fwd needs for `desc`: u, q, k, v and the
  * [o | m] concat buffer, all bf16 (16 * N * D bytes at F = 3 D), plus a fixed
- * 128 MiB of fp32 scratch for the split tails of the GEMMs. */
+ * 128 MiB of fp32 scratch for the split tails of the GEMMs (and the split
+ * partials of attention) and 4 KiB of attention counters.
+ * After a call the workspace holds the block's intermediates, at offsets that
+ * are multiples of R = (N * D * 2 rounded up to 256 bytes):
+ *   0:   u   bf16 [N, D]      the modulated input
+ *   R:   q   bf16 [N, H, d]   after QK RMSNorm and RoPE, multiplied by
+ *                             (float)(1 / sqrt(128)) * (float)log2(e)
+ *   2R:  k   bf16 [N, H, d]   after QK RMSNorm and RoPE
+ *   3R:  v   bf16 [N, H, d]
+ *   4R:  [o | m] bf16 [N, D + F]  attention output, then the SwiGLU product
+ * (for inspection and tests; the layout is part of this contract). */
 int dit_block_workspace_bytes(const dit_block_desc* desc, size_t* bytes);
 
 /* One parallel block forward (the whole chain above).
@@ -157,6 +167,22 @@ int dit_block_noalloc_scratch_bytes(size_t* bytes);
  * product with v.  softmax_scale must be finite and > 0 (1/sqrt(d) for the block). */
 int dit_attn_fwd(int32_t n_tokens, int32_t n_heads, int32_t head_dim, const void* q,
                  const void* k, const void* v, void* o, float softmax_scale, hipStream_t stream);
+
+/* Bytes of device workspace dit_attn_fwd_ws needs (a fixed size, about 71 MB,
+ * for any valid shape; the shape is checked as in dit_attn_fwd). */
+int dit_attn_workspace_bytes(int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                             size_t* bytes);
+
+/* dit_attn_fwd with a workspace, which lets it balance the work over the
+ * CUs the way the block's attention does: when there are more (head, 256-query)
+ * items than CUs, each CU takes an equal share of the key tiles of all
+ * items, and an item cut between two shares is merged from two fp32
+ * partials kept in the workspace.  Same result definition and errors as
+ * dit_attn_fwd, plus DIT_ERR_WORKSPACE (null or too small) and DIT_ERR_ARG
+ * (workspace overlapping q, k, v or o). */
+int dit_attn_fwd_ws(int32_t n_tokens, int32_t n_heads, int32_t head_dim, const void* q,
+                    const void* k, const void* v, void* o, float softmax_scale, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
 
 /* In-place per-head QK RMSNorm (when q_scale and k_scale are both non-null)
  * followed by 4-axis RoPE on q and k ("How it works": axes t, h, w, l each

@@ -153,7 +153,7 @@ def block_ref(x, mod, pos, w_in, w_out, q_scale, k_scale, n_tokens: Sequence[int
     rows (keys and values still come from every token).
     Returns y, r (the branch before the gate), o (attention out, [n, D]),
     m (SwiGLU out), q (after norm and RoPE, [n, H, d]) at the selected rows,
-    and k (after norm and RoPE) and u (modulated input) at every row.
+    and k (after norm and RoPE), v and u (modulated input) at every row.
     """
     def f(a):
         a = np.asarray(a)
@@ -184,7 +184,7 @@ def block_ref(x, mod, pos, w_in, w_out, q_scale, k_scale, n_tokens: Sequence[int
     s = stream_index(n_tokens)[sel]
     gate = np.ones_like(r) if flags & FLAG_NO_GATE else mod[s, 2, :]
     y = gate * r if flags & FLAG_NO_RESIDUAL else x[sel] + gate * r
-    return {"y": y, "r": r, "o": o, "m": m, "q": q, "k": k, "u": u}
+    return {"y": y, "r": r, "o": o, "m": m, "q": q, "k": k, "v": v, "u": u}
 
 
 def rel_l2(a, b) -> float:

@@ -61,10 +61,12 @@ def test_workspace_bytes(lib):
     assert rc == OK
     N, D, F = 4256, 3072, 9216
     # u, q, k, v [N, D] and [o | m] [N, D + F] in bf16, plus the fixed fp32
-    # scratch of the GEMMs' split tail (two 256 x 256 tiles for each of 256 pieces)
+    # scratch of the GEMMs' split tail (two 256 x 256 tiles for each of 256
+    # pieces; attention's split partials reuse it) and 1024 attention counters
     split = 2 * 256 * 256 * 256 * 4
-    assert n >= 2 * (4 * N * D + N * (D + F)) + split
-    assert n < 2 * (4 * N * D + N * (D + F)) + split + 6 * 256
+    counters = 1024 * 4
+    assert n >= 2 * (4 * N * D + N * (D + F)) + split + counters
+    assert n < 2 * (4 * N * D + N * (D + F)) + split + counters + 7 * 256
     rc, n8352 = ws(lib, ops.make_desc([4096, 4096, 160]))
     assert rc == OK and n8352 > 400e6
     assert ws(lib, ops.make_desc([0]))[0] == OK
@@ -147,6 +149,26 @@ def test_attn_host_errors(lib):
     assert f(100, 24, 128, a, b, cc, o, float("inf"), None) == ARG
     assert f(100, 24, 128, a, b, cc, c(P + 4096), 0.1, None) == ARG   # o overlaps q
     assert f(0, 24, 128, None, None, None, None, 0.1, None) == OK      # empty call
+
+
+def test_attn_ws_host_errors(lib):
+    c = ctypes.c_void_p
+    n = ctypes.c_size_t(0)
+    assert lib.dit_attn_workspace_bytes(4256, 24, 128, ctypes.byref(n)) == OK
+    need = n.value
+    # the split partials of up to 256 shares (two fp32 parts of 256 queries x
+    # 128 dims plus row sums and maxima each) and their counters
+    assert need >= 256 * 2 * 8 * 17 * 64 * 16 + 256 * 4
+    assert lib.dit_attn_workspace_bytes(4256, 24, 64, ctypes.byref(n)) == UNSUP
+    assert lib.dit_attn_workspace_bytes(4256, 24, 128, None) == NULL
+    f = lib.dit_attn_fwd_ws
+    a, b, cc, o, w = (c(P + (i << 30)) for i in range(5))
+    assert f(100, 24, 128, a, b, cc, o, 0.1, None, need, None) == NULL
+    assert f(100, 24, 128, a, b, cc, o, 0.1, c(BAD + (4 << 30)), need, None) == ALIGN
+    assert f(100, 24, 128, a, b, cc, o, 0.1, w, need - 1, None) == WS
+    assert f(100, 24, 128, a, b, cc, o, 0.1, c(P + (3 << 30) + 4096), need, None) == ARG
+    assert f(100, 24, 64, a, b, cc, o, 0.1, w, need, None) == UNSUP
+    assert f(0, 24, 128, None, None, None, None, 0.1, None, 0, None) == OK
 
 
 def test_rope_host_errors(lib):

@@ -121,6 +121,41 @@ def test_attn_parity_sampled(N, logit_std):
     assert oracle.rel_l2(widen(o)[rows], ref) <= TOL_ATTN
 
 
+# dit_attn_fwd_ws splits the work into one equal share of key tiles per CU
+# when there are more (head, 256-query) items than CUs; an item cut between
+# two shares is merged from two fp32 partials by whichever share ends last.
+# On a 256-CU device: 3,000 tokens x 24 heads = 288 items (almost every item
+# cut, checked on every row), 4,256 x 24 = 408 items (the block's shape),
+# 8,352 x 24 = 792, and 16,484 tokens x 4 heads = 260 items of 258 key tiles
+# against shares of 262 (every share holds the tail of one item and the head
+# of the next).  logit_std 1 to 8 runs the running-max merge with references
+# far apart.
+@pytest.mark.parametrize("N,H,logit_std,all_rows", [(3000, 24, 2.0, True), (4256, 24, 1.0, False),
+                                                    (4256, 24, 8.0, False),
+                                                    (8352, 24, 2.0, False),
+                                                    (16484, 4, 4.0, False)])
+def test_attn_ws_split_parity(N, H, logit_std, all_rows):
+    d = inputs.make_attn_inputs(N, H, 128, seed=8, logit_std=logit_std)
+    log(f"attn_ws N={N} H={H} logit_std={logit_std}")
+    dv = to_dev(d)
+    o = ops.attn_fwd_ws(dv["q"], dv["k"], dv["v"])
+    torch.cuda.synchronize()
+    if all_rows:
+        rows = np.arange(N)
+    else:
+        rows = np.unique(np.concatenate([[0, 1, 255, 256, N - 1, N - 2],
+                                         np.random.default_rng(2).choice(N, 90, replace=False)]))
+    q, k, v = (oracle.widen_bf16(d[n]) for n in ("q", "k", "v"))
+    ref = oracle.attention_ref(q[rows], k, v, 128 ** -0.5)
+    e = oracle.rel_l2(widen(o)[rows], ref)
+    log(f"  relL2 {e:.3e}")
+    assert e <= TOL_ATTN
+    # the merge is symmetric in the two parts: a second run is bitwise equal
+    o2 = ops.attn_fwd_ws(dv["q"], dv["k"], dv["v"])
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+
+
 def test_attn_softmax_scale_argument():
     N = 300
     d = inputs.make_attn_inputs(N, 24, 128, seed=7)

@@ -10,7 +10,7 @@ steps gives per-stage times from HIP events the library records on the work
 stream between its kernels.  The fp64 CPU oracle of the same block
 is timed once on the host as a baseline and its output gives the parity of
 the timed configuration (y, and the branch r read with the residual and gate
-switched off); dit_attn_fwd alone is checked at sampled query rows against
+switched off); attention alone (dit_attn_fwd_ws) is checked at sampled query rows against
 the oracle's attention on the same seeded bf16 q, k, v.  A secondary field times one guided denoise step of
 the two-stage stack (c5) through dit_stack_fwd and the flow-matching sampler
 at the same shapes (`--no-stack` skips both), and
@@ -348,12 +348,13 @@ def stage1_c3(torch, configs, ops, steps: int, warmup: int) -> dict:
 
 
 def attn_parity(torch, oracle, inputs, ops, N: int, n_rows: int = 64) -> dict:
-    """dit_attn_fwd alone at N tokens on seeded bf16 q, k, v (24 x 128 heads),
-    against the oracle's attention on the same bf16 values, at sampled query
-    rows (the oracle computes each row against all N keys)."""
+    """Attention alone at N tokens (dit_attn_fwd_ws: the block's schedule, one
+    equal share of the key tiles per CU) on seeded bf16 q, k, v (24 x 128
+    heads), against the oracle's attention on the same bf16 values, at sampled
+    query rows (the oracle computes each row against all N keys)."""
     d = inputs.make_attn_inputs(N, 24, 128, seed=6, logit_std=1.0)
     q, k, v = (ops.to_device_bf16(d[n]) for n in ("q", "k", "v"))
-    o = ops.attn_fwd(q, k, v)
+    o = ops.attn_fwd_ws(q, k, v)
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([[0, N - 1],
                                      np.random.default_rng(1).choice(N, n_rows, replace=False)]))

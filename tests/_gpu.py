@@ -28,11 +28,22 @@ def widen(t):
     return oracle.widen_bf16(ops.to_host_bits(t))
 
 
-def run_block(dv, cfg, flags=0, y=None):
+def poisoned_workspace(desc):
+    """A workspace whose every byte is 0xFF (bf16 NaN patterns), so that an
+    output or intermediate the kernels fail to write shows up as NaN instead
+    of a stale value left by an earlier call in the same memory."""
+    return ops.alloc_workspace(desc).fill_(0xFF)
+
+
+def run_block(dv, cfg, flags=0, y=None, workspace=None):
     desc = ops.make_desc(cfg.n_tokens, cfg.width, cfg.n_heads, cfg.head_dim, cfg.mlp_hidden,
                          flags=flags)
+    if y is None:
+        y = torch.full_like(dv["x"], float("nan"))
+    if workspace is None:
+        workspace = poisoned_workspace(desc)
     y = ops.block_fwd(dv["x"], dv["mod"], dv["pos"], dv["w_in"], dv["w_out"], dv["q_scale"],
-                      dv["k_scale"], desc, y=y)
+                      dv["k_scale"], desc, y=y, workspace=workspace)
     torch.cuda.synchronize()
     return y
 

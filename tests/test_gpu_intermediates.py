@@ -35,7 +35,7 @@ import torch
 import oracle
 from flow_matching_diffusion_adaln_amd import configs, inputs, ops
 
-from _gpu import block_config, require_gpu, sample_rows, to_dev
+from _gpu import block_config, poisoned_workspace, require_gpu, sample_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -104,7 +104,7 @@ def check_intermediates(cfg, seed, rows=None):
     d = inputs.make_block_inputs(cfg, seed=seed)
     dv = to_dev(d)
     desc = ops.make_desc(cfg.n_tokens, cfg.width, cfg.n_heads, cfg.head_dim, cfg.mlp_hidden)
-    ws = ops.alloc_workspace(desc)
+    ws = poisoned_workspace(desc)
     log(f"intermediates {cfg.name} N={cfg.N} rows={'all' if rows is None else len(rows)}")
     ops.block_fwd(dv["x"], dv["mod"], dv["pos"], dv["w_in"], dv["w_out"], dv["q_scale"],
                   dv["k_scale"], desc, workspace=ws)

@@ -80,3 +80,16 @@ def test_attention_45k_sampled():
     e = oracle.rel_l2(got, want)
     log(f"attention N={N} sampled rows={len(rows)} relL2 {e:.3e}")
     assert e <= TOL_ATTN
+
+
+def test_block_edit2048_sampled():
+    # the long edit the bench times: 2048^2 image (16,384 tokens) | one
+    # 2048^2 reference sharing its (h, w) with l = 1 (16,384) | 160 text,
+    # 32,928 tokens in three streams; attention is then 62% of the FLOPs and
+    # its balanced split cuts many items
+    require_gpu()
+    cfg = configs.EDIT_2048
+    d = inputs.make_block_inputs(cfg, seed=8)
+    rows = sample_rows(cfg, n_random=24)
+    log(f"block {cfg.name} N={cfg.N} rows={len(rows)}")
+    check(cfg, d, rows)

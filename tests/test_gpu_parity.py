@@ -138,7 +138,11 @@ def test_attn_ws_split_parity(N, H, logit_std, all_rows):
     d = inputs.make_attn_inputs(N, H, 128, seed=8, logit_std=logit_std)
     log(f"attn_ws N={N} H={H} logit_std={logit_std}")
     dv = to_dev(d)
-    o = ops.attn_fwd_ws(dv["q"], dv["k"], dv["v"])
+    # output and workspace start as NaN patterns, so a cut item that nobody
+    # finished shows up
+    ws = torch.full((ops.attn_workspace_bytes(N, H),), 0xFF, dtype=torch.uint8, device="cuda")
+    o = ops.attn_fwd_ws(dv["q"], dv["k"], dv["v"], o=torch.full_like(dv["q"], float("nan")),
+                        workspace=ws)
     torch.cuda.synchronize()
     if all_rows:
         rows = np.arange(N)
@@ -151,7 +155,8 @@ def test_attn_ws_split_parity(N, H, logit_std, all_rows):
     log(f"  relL2 {e:.3e}")
     assert e <= TOL_ATTN
     # the merge is symmetric in the two parts: a second run is bitwise equal
-    o2 = ops.attn_fwd_ws(dv["q"], dv["k"], dv["v"])
+    o2 = ops.attn_fwd_ws(dv["q"], dv["k"], dv["v"], o=torch.full_like(dv["q"], float("nan")),
+                         workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
 

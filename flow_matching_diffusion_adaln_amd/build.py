@@ -15,8 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdit.so")
-SOURCES = ["abi.cpp", "adaln.hip", "rope.hip", "attn.hip", "gemm.hip", "cfg.hip", "sampler.hip",
-           "quant.hip"]
+SOURCES = ["abi.cpp", "adaln.hip", "rope.hip", "attn.hip", "gemm.hip", "thin.hip", "cfg.hip",
+           "sampler.hip", "quant.hip"]
 ARCH = "gfx950"
 
 

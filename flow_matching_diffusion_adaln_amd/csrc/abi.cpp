@@ -71,19 +71,23 @@ int check_desc(const dit_block_desc* d, Shape* sh) {
 struct Workspace {
   uint16_t *u, *q, *k, *v, *cat;
   float* partial;  // GEMM split-K partial tiles; attention's split partials
-  int* attn_cnt;   // attention's split counters, zeroed by the AdaLN launch
+  int* attn_cnt;   // kCounters ints, zeroed by the AdaLN launch: attention's split
+                   // counters, then the short-sequence output projection's
   size_t bytes;
 };
 
-// Attention counters in the block workspace (one per cut between two CU
-// shares; more than any GPU has CUs).
-constexpr int kAttnCounters = 1024;
+// Counters in the block workspace: attention's (one per cut between two CU
+// shares; more than any GPU has CUs), then one per 128 output columns of the
+// short-sequence output projection.
+constexpr int kAttnCounters = 512;
+constexpr int kThinCounters = 512;
+constexpr int kCounters = kAttnCounters + kThinCounters;
 
 // Bytes of the block workspace for N tokens of width D and MLP hidden F (the
 // sum of the regions `layout` places).
 constexpr size_t block_ws_bytes(size_t N, size_t D, size_t F) {
   return 4 * round_up(N * D * 2) + round_up(N * (D + F) * 2) + round_up(dit::kGemmPartialBytes) +
-         round_up(kAttnCounters * sizeof(int));
+         round_up(kCounters * sizeof(int));
 }
 
 Workspace layout(const Shape& s, void* base) {
@@ -105,7 +109,7 @@ Workspace layout(const Shape& s, void* base) {
   w.partial = reinterpret_cast<float*>(p + off);
   off += round_up(dit::kGemmPartialBytes);
   w.attn_cnt = reinterpret_cast<int*>(p + off);
-  off += round_up(kAttnCounters * sizeof(int));
+  off += round_up(kCounters * sizeof(int));
   w.bytes = off;
   return w;
 }
@@ -194,7 +198,7 @@ int block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const 
   const uint16_t* mb = static_cast<const uint16_t*>(mod);
   if ((rc = mark(DIT_STAGE_ADALN))) return rc;
   if ((rc = hip_status(dit::launch_adaln(xb, mb, w.u, s.N, s.D, s.e0, s.e1, desc->ln_eps,
-                                         stream, w.attn_cnt, kAttnCounters))))
+                                         stream, w.attn_cnt, kCounters))))
     return rc;
   if ((rc = mark(DIT_STAGE_GEMM_IN))) return rc;
   // the input projection applies the QK RMSNorm and RoPE in its epilogue, so
@@ -216,7 +220,8 @@ int block_fwd(const dit_block_desc* desc, const void* x, const void* mod, const 
   if ((rc = mark(DIT_STAGE_GEMM_OUT))) return rc;
   if ((rc = hip_status(dit::launch_gemm_out(w.cat, static_cast<const uint16_t*>(w_out), s.N,
                                             s.D, s.F, xb, mb, static_cast<uint16_t*>(y), s.e0,
-                                            s.e1, desc->flags, w.partial, stream))))
+                                            s.e1, desc->flags, w.partial, stream,
+                                            w.attn_cnt + kAttnCounters, kThinCounters))))
     return rc;
   return mark(DIT_N_STAGES);
 }
@@ -279,7 +284,7 @@ int block_fwd_fp8(const dit_block_desc* desc, const void* x, const void* mod, co
   if ((rc = mark(DIT_STAGE_ADALN))) return rc;
   if ((rc = hip_status(dit::launch_adaln_fp8(xb, mb, w.u8, w.u_scale, s.N, s.D, s.e0, s.e1,
                                              desc->ln_eps, stream, w.base.attn_cnt,
-                                             kAttnCounters))))
+                                             kCounters))))
     return rc;
   if ((rc = mark(DIT_STAGE_GEMM_IN))) return rc;
   if ((rc = hip_status(dit::launch_gemm_in_fp8(

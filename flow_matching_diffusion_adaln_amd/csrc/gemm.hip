@@ -1181,6 +1181,9 @@ hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D,
                           const int32_t* pos, const uint16_t* q_scale, const uint16_t* k_scale,
                           float theta, float qk_eps, float q_mul, float* partial,
                           hipStream_t stream) {
+  if (thin_fits(M, D, F))
+    return launch_thin_in(u, w_in, M, D, F, q, k, v, cat, pos, q_scale, k_scale, theta, qk_eps,
+                          q_mul, stream);
   GemmArgs g = in_args(u, w_in, M, D, F, q, k, v, cat, pos, q_scale, k_scale, theta, qk_eps,
                        partial);
   g.q_mul = q_mul;
@@ -1189,7 +1192,11 @@ hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D,
 
 hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, int D, int F,
                            const uint16_t* x, const uint16_t* mod, uint16_t* y, int e0, int e1,
-                           uint32_t flags, float* partial, hipStream_t stream) {
+                           uint32_t flags, float* partial, hipStream_t stream, int* counters,
+                           int n_counters) {
+  if (thin_fits(M, D, F))
+    return launch_thin_out(cat, w_out, M, D, F, x, mod, y, e0, e1, flags, partial,
+                           partial ? kGemmPartialBytes : 0, counters, n_counters, stream);
   return launch<EPI_OUT, false>(out_args(cat, w_out, M, D, F, x, mod, y, e0, e1, flags, partial),
                                 stream);
 }

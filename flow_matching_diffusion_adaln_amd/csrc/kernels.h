@@ -70,9 +70,32 @@ hipError_t launch_gemm_in(const uint16_t* u, const uint16_t* w_in, int M, int D,
                           float theta, float qk_eps, float q_mul, float* partial,
                           hipStream_t stream);
 
+// counters (may be null): n_counters zeroed ints that let a short sequence
+// run the weight-streaming output projection with its K split (see below)
 hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, int D, int F,
                            const uint16_t* x, const uint16_t* mod, uint16_t* y, int e0, int e1,
-                           uint32_t flags, float* partial, hipStream_t stream);
+                           uint32_t flags, float* partial, hipStream_t stream,
+                           int* counters = nullptr, int n_counters = 0);
+
+// Projections of short sequences (at most kThinMaxTokens tokens) as weight
+// streams: a workgroup per 128 weight rows, every token in the MFMAs' other
+// operand, epilogues fused (thin.hip).  thin_fits: the shapes they take.
+// The output projection cuts K into pieces whose fp32 partials
+// (thin_partial_bytes) are summed by the last piece to arrive, counted in
+// `counters` (D / 128 ints, zero at launch, left zero); with too little
+// scratch it runs whole columns instead.
+constexpr int kThinMaxTokens = 128;
+constexpr int kThinMaxPieces = 32;
+bool thin_fits(int M, int D, int F);
+size_t thin_partial_bytes(int M, int D, int pieces);
+hipError_t launch_thin_in(const uint16_t* u, const uint16_t* w_in, int M, int D, int F,
+                          uint16_t* q, uint16_t* k, uint16_t* v, uint16_t* cat,
+                          const int32_t* pos, const uint16_t* q_scale, const uint16_t* k_scale,
+                          float theta, float qk_eps, float q_mul, hipStream_t stream);
+hipError_t launch_thin_out(const uint16_t* cat, const uint16_t* w_out, int M, int D, int F,
+                           const uint16_t* x, const uint16_t* mod, uint16_t* y, int e0, int e1,
+                           uint32_t flags, float* partial, size_t partial_bytes, int* counters,
+                           int n_counters, hipStream_t stream);
 
 // FP8 projections: e4m3 operands with rowwise scales (u8 / cat8 rows scaled
 // by u_scale / cat_scale, weight rows by w_*_scale), epilogues as above.

@@ -240,12 +240,33 @@ def test_block_parity_single_token():
     check_block(block_config("one", (1,), 92))
 
 
-# At most 128 tokens the projections run 128-row tiles, every tile split
-# along K: exactly one full row of tiles (128), a last 32-row block that is
-# only partly inside M (97), and two streams (100 image + 28 text).
+# At most 128 tokens the projections stream their weights: a workgroup per
+# 128 weight rows with every token in the other MFMA operand (4 blocks of 32
+# at 128 tokens, a last block only partly inside M at 97), the output
+# projection's K cut into pieces merged by the last to arrive, and two
+# streams (100 image + 28 text) for the per-stream gate.
 @pytest.mark.parametrize("n_tokens,cid", [((128,), 97), ((97,), 98), ((100, 28), 99)])
 def test_block_parity_short_128_row_tiles(n_tokens, cid):
     check_block(block_config(f"short{sum(n_tokens)}", n_tokens, cid))
+
+
+def test_block_parity_short_qk_scales():
+    # QK-norm scales away from one through the short-sequence input
+    # projection's norm + RoPE epilogue (the head's sum of squares meets
+    # across its four waves in LDS)
+    check_block(block_config("short80s", (80,), 102), seed=5, scaled=True)
+
+
+# The short-sequence projections at width 2,048 (16 heads) with SwiGLU 6,144
+# (K of 2,048 and 8,192, whole numbers of the 4-stage ring's 256 columns),
+# and with SwiGLU 6,016, whose output-projection K = 8,064 is not, so the
+# block takes the tiled GEMMs with every tile split along K and the separate
+# norm + RoPE pass.
+@pytest.mark.parametrize("width,heads,mlp,cid", [(2048, 16, 6144, 100), (2048, 16, 6016, 101)])
+def test_block_parity_short_other_widths(width, heads, mlp, cid):
+    cfg = block_config(f"short_w{width}", (80,), cid, width=width, n_heads=heads,
+                       mlp_hidden=mlp)
+    check_block(cfg)
 
 
 # On a 256-CU device these token counts make the GEMMs cut their last, partly

@@ -120,7 +120,10 @@ def stack_c5(torch, configs, ops, steps: int, warmup: int) -> dict:
     (5 image + 5 text stage-1 blocks, 28 joint blocks, CFG scale 4) through
     dit_stack_fwd, each block with its own random weights generated on the
     device (38 sets, 9.3 GB).  The image stage-1 blocks are shared by both
-    guidance branches, so the executed FLOPs are below two full forwards."""
+    guidance branches, so the executed FLOPs are below two full forwards.
+    Timed four ways: eager, with the stage-1 text blocks on the library's
+    second stream (DIT_STACK_TEXT_SIDE_STREAM), and both as replays of one
+    captured HIP graph."""
     sc = configs.C5
     D, F, d = configs.WIDTH, configs.MLP_HIDDEN, configs.HEAD_DIM
     n_img, n_txt = sc.image_side * sc.image_side, sc.n_text
@@ -143,17 +146,37 @@ def stack_c5(torch, configs, ops, steps: int, warmup: int) -> dict:
     x_c, x_n = rnd((n_txt, D), 1.0), rnd((n_txt, D), 1.0)
     from flow_matching_diffusion_adaln_amd import inputs
     pos = torch.from_numpy(inputs.positions(cfg_joint)).cuda()
-    desc = ops.make_stack_desc(n_img, n_txt, sc.n_stage1, sc.n_stage1, sc.n_joint, sc.cfg_scale)
-    ws = torch.empty(ops.stack_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
     v = torch.empty((n_img, D), dtype=torch.bfloat16, device="cuda")
-    for _ in range(warmup):
-        ops.stack_fwd(desc, x_img, x_c, x_n, pos, blocks, v_img=v, workspace=ws)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        ops.stack_fwd(desc, x_img, x_c, x_n, pos, blocks, v_img=v, workspace=ws)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    def timed(side, graph):
+        """ms per denoise step: eager calls or replays of one captured call;
+        side: the stage-1 text blocks on the library's second stream."""
+        desc = ops.make_stack_desc(n_img, n_txt, sc.n_stage1, sc.n_stage1, sc.n_joint,
+                                   sc.cfg_scale, side_stream=side)
+        ws = torch.empty(ops.stack_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+        call = lambda: ops.stack_fwd(desc, x_img, x_c, x_n, pos, blocks, v_img=v, workspace=ws)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                call()
+            call = g.replay
+            call()
+            torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        del ws
+        return ms
+
+    ms = timed(False, False)
+    ms_side = timed(True, False)
+    ms_graph = timed(False, True)
+    ms_side_graph = timed(True, True)
     flop_exec = (sc.n_stage1 * cfg_img.flop() + 2 * sc.n_stage1 * cfg_txt.flop()
                  + 2 * sc.n_joint * cfg_joint.flop())
     flop_nominal = 2 * sc.n_stage1 * (cfg_img.flop() + cfg_txt.flop()) + 2 * sc.n_joint * cfg_joint.flop()
@@ -163,6 +186,9 @@ def stack_c5(torch, configs, ops, steps: int, warmup: int) -> dict:
                     f"stage-1 blocks, {sc.n_joint} joint blocks ({n_img + n_txt}), CFG pair "
                     f"(scale {sc.cfg_scale}); image stage-1 shared by both branches",
         "ms_per_denoise_step": round(ms, 3),
+        "ms_text_side_stream": round(ms_side, 3),
+        "ms_hip_graph": round(ms_graph, 3),
+        "ms_text_side_stream_hip_graph": round(ms_side_graph, 3),
         "tflops_executed": round(flop_exec / (ms * 1e-3) / 1e12, 2),
         "gflop_executed": round(flop_exec / 1e9, 1),
         "gflop_two_full_forwards": round(flop_nominal / 1e9, 1),

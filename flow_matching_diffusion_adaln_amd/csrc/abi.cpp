@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "dit.h"
 #include "kernels.h"
@@ -353,12 +354,50 @@ int check_stack(const dit_stack_desc* d, Shape* joint, size_t* bytes) {
       kMaxStackBlocks)
     return DIT_ERR_SHAPE;
   if (!isfinite(d->cfg_scale)) return DIT_ERR_ARG;
+  if (d->flags & ~DIT_STACK_TEXT_SIDE_STREAM) return DIT_ERR_ARG;
   const dit_block_desc jd = joint_desc(d);
   const int rc = check_desc(&jd, joint);
   if (rc != DIT_OK) return rc;
   const size_t act = round_up((size_t)joint->N * joint->D * 2);
   *bytes = layout(*joint, nullptr).bytes + 2 * act;
+  if (d->flags & DIT_STACK_TEXT_SIDE_STREAM) {
+    Shape ts = *joint;
+    ts.N = d->n_txt;
+    *bytes += layout(ts, nullptr).bytes;
+  }
   return DIT_OK;
+}
+
+// The side stream of DIT_STACK_TEXT_SIDE_STREAM and its fork / join events,
+// one set per device, created on first use and kept until the process ends.
+struct SideStream {
+  hipStream_t stream;
+  hipEvent_t fork, join;
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+bool g_side_ok[kMaxDevices];
+
+// The current device's set, or null with *rc set.
+const SideStream* side_stream(int* rc) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *rc = DIT_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  if (!g_side_ok[dev]) {
+    SideStream s{};
+    if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess) {
+      *rc = DIT_ERR_HIP;
+      return nullptr;
+    }
+    g_side[dev] = s;
+    g_side_ok[dev] = true;
+  }
+  return &g_side[dev];
 }
 
 int check_params(const dit_block_params& p) {
@@ -433,6 +472,7 @@ int check_model(const dit_model_desc* d, Shape* js, size_t* bytes) {
   size_t stack_bytes = 0;
   int rc = check_stack(&d->stack, js, &stack_bytes);
   if (rc != DIT_OK) return rc;
+  if (d->stack.flags != 0) return DIT_ERR_ARG;  // text blocks run once, in prepare
   if (d->latent_ch <= 0 || d->text_dim <= 0) return DIT_ERR_SHAPE;
   if (d->latent_ch % 32 != 0 || d->latent_ch > 8192 || d->text_dim % 16 != 0 ||
       d->text_dim > (1 << 20))
@@ -729,44 +769,86 @@ int dit_stack_fwd(const dit_stack_desc* desc, const void* x_img, const void* x_r
   const dit_block_params* br = bi + desc->n_img_blocks;
   const dit_block_params* bt = br + desc->n_ref_blocks;
   const dit_block_params* bj = bt + desc->n_txt_blocks;
+  auto run_on = [&](const dit_block_desc& d, const dit_block_params& p, char* h,
+                    const int32_t* ps, char* ws, size_t ws_bytes, hipStream_t st) -> int {
+    return block_fwd(&d, h, p.mod, ps, p.w_in, p.w_out, p.q_scale, p.k_scale, h, ws, ws_bytes, st,
+                     nullptr);
+  };
   auto run = [&](const dit_block_desc& d, const dit_block_params& p, char* h,
                  const int32_t* ps) -> int {
-    return block_fwd(&d, h, p.mod, ps, p.w_in, p.w_out, p.q_scale, p.k_scale, h, wsp, block_ws,
-                     stream, nullptr);
+    return run_on(d, p, h, ps, wsp, block_ws, stream);
   };
   auto copy = [&](void* dst, const void* src, size_t n) -> int {
     return hip_status(hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, stream));
   };
-
-  // stage 1, image and reference: shared by both branches
-  if ((rc = copy(xc, x_img, img_bytes)) != DIT_OK) return rc;
-  for (int i = 0; i < desc->n_img_blocks; ++i)
-    if ((rc = run(di, bi[i], xc, pos)) != DIT_OK) return rc;
-  if (refs) {
-    if ((rc = copy(xc + img_bytes, x_ref, ref_bytes)) != DIT_OK) return rc;
-    for (int i = 0; i < desc->n_ref_blocks; ++i)
-      if ((rc = run(dr, br[i], xc + img_bytes, pos_ref)) != DIT_OK) return rc;
-  }
-  if (guided && (rc = copy(xn, xc, pre_bytes)) != DIT_OK) return rc;
-  // stage 1, text, then the joint blocks, per branch (in place on
-  // [image | reference | text])
-  auto branch = [&](char* h, const void* x_txt) -> int {
-    int r = copy(h + pre_bytes, x_txt, txt_bytes);
-    if (r != DIT_OK) return r;
-    for (int i = 0; i < desc->n_txt_blocks; ++i)
-      if ((r = run(dt, bt[i], h + pre_bytes, pos_txt)) != DIT_OK) return r;
+  auto joint = [&](char* h) -> int {
     for (int i = 0; i < desc->n_joint_blocks; ++i)
-      if ((r = run(dj, bj[i], h, pos)) != DIT_OK) return r;
+      if ((rc = run(dj, bj[i], h, pos)) != DIT_OK) return rc;
     return DIT_OK;
   };
-  if ((rc = branch(xc, x_txt_cond)) != DIT_OK) return rc;
-  if (!guided) return copy(v_img, xc, img_bytes);
-  if ((rc = branch(xn, x_txt_neg)) != DIT_OK) return rc;
-  return hip_status(dit::launch_cfg_combine(reinterpret_cast<const uint16_t*>(xc),
-                                            reinterpret_cast<const uint16_t*>(xn),
-                                            static_cast<uint16_t*>(v_img),
-                                            (long long)desc->n_img * js.D, desc->cfg_scale,
-                                            stream));
+  auto finish = [&]() -> int {
+    if ((rc = joint(xc)) != DIT_OK) return rc;
+    if (!guided) return copy(v_img, xc, img_bytes);
+    if ((rc = joint(xn)) != DIT_OK) return rc;
+    return hip_status(dit::launch_cfg_combine(reinterpret_cast<const uint16_t*>(xc),
+                                              reinterpret_cast<const uint16_t*>(xn),
+                                              static_cast<uint16_t*>(v_img),
+                                              (long long)desc->n_img * js.D, desc->cfg_scale,
+                                              stream));
+  };
+  // stage 1, image and reference: shared by both branches
+  auto stage1_shared = [&]() -> int {
+    if ((rc = copy(xc, x_img, img_bytes)) != DIT_OK) return rc;
+    for (int i = 0; i < desc->n_img_blocks; ++i)
+      if ((rc = run(di, bi[i], xc, pos)) != DIT_OK) return rc;
+    if (refs) {
+      if ((rc = copy(xc + img_bytes, x_ref, ref_bytes)) != DIT_OK) return rc;
+      for (int i = 0; i < desc->n_ref_blocks; ++i)
+        if ((rc = run(dr, br[i], xc + img_bytes, pos_ref)) != DIT_OK) return rc;
+    }
+    if (guided && (rc = copy(xn, xc, pre_bytes)) != DIT_OK) return rc;
+    return DIT_OK;
+  };
+
+  if (desc->flags & DIT_STACK_TEXT_SIDE_STREAM) {
+    // The text rows of each branch are filled and the fork recorded on the
+    // caller's stream; the side stream runs both branches' text blocks (in
+    // place on the text rows, with a block workspace of its own) while the
+    // caller's stream runs the image and reference blocks on the other rows;
+    // the joint blocks wait for the join.
+    const SideStream* side = side_stream(&rc);
+    if (!side) return rc;
+    Shape ts = js;
+    ts.N = desc->n_txt;
+    char* wst = xn + act;
+    const size_t wst_bytes = layout(ts, nullptr).bytes;
+    if ((rc = copy(xc + pre_bytes, x_txt_cond, txt_bytes)) != DIT_OK) return rc;
+    if (guided && (rc = copy(xn + pre_bytes, x_txt_neg, txt_bytes)) != DIT_OK) return rc;
+    if ((rc = hip_status(hipEventRecord(side->fork, stream))) != DIT_OK ||
+        (rc = hip_status(hipStreamWaitEvent(side->stream, side->fork, 0))) != DIT_OK)
+      return rc;
+    for (int b = 0; b < (guided ? 2 : 1); ++b) {
+      char* h = (b ? xn : xc) + pre_bytes;
+      for (int i = 0; i < desc->n_txt_blocks; ++i)
+        if ((rc = run_on(dt, bt[i], h, pos_txt, wst, wst_bytes, side->stream)) != DIT_OK)
+          return rc;
+    }
+    if ((rc = hip_status(hipEventRecord(side->join, side->stream))) != DIT_OK) return rc;
+    if ((rc = stage1_shared()) != DIT_OK) return rc;
+    if ((rc = hip_status(hipStreamWaitEvent(stream, side->join, 0))) != DIT_OK) return rc;
+    return finish();
+  }
+
+  if ((rc = stage1_shared()) != DIT_OK) return rc;
+  // stage 1, text, per branch (in place on the text rows of [image |
+  // reference | text])
+  for (int b = 0; b < (guided ? 2 : 1); ++b) {
+    char* h = b ? xn : xc;
+    if ((rc = copy(h + pre_bytes, b ? x_txt_neg : x_txt_cond, txt_bytes)) != DIT_OK) return rc;
+    for (int i = 0; i < desc->n_txt_blocks; ++i)
+      if ((rc = run(dt, bt[i], h + pre_bytes, pos_txt)) != DIT_OK) return rc;
+  }
+  return finish();
 }
 
 int dit_flow_sigmas(int32_t n_steps, double alpha, double* sigmas) {

@@ -66,7 +66,11 @@ class StackDesc(ctypes.Structure):
         ("ln_eps", ctypes.c_float),
         ("qk_eps", ctypes.c_float),
         ("cfg_scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
     ]
+
+
+DIT_STACK_TEXT_SIDE_STREAM = 1
 
 
 class BlockParams(ctypes.Structure):
@@ -352,7 +356,9 @@ def make_stack_desc(n_img: int, n_txt: int, n_img_blocks: int, n_txt_blocks: int
                     n_joint_blocks: int, cfg_scale: float, n_ref: int = 0, n_ref_blocks: int = 0,
                     width: int = configs.WIDTH, n_heads: int = configs.N_HEADS,
                     head_dim: int = configs.HEAD_DIM,
-                    mlp_hidden: int = configs.MLP_HIDDEN) -> StackDesc:
+                    mlp_hidden: int = configs.MLP_HIDDEN, side_stream: bool = False) -> StackDesc:
+    """side_stream: run the stage-1 text blocks on the library's second stream
+    (DIT_STACK_TEXT_SIDE_STREAM)."""
     d = StackDesc()
     d.n_img, d.n_ref, d.n_txt = n_img, n_ref, n_txt
     d.n_img_blocks, d.n_ref_blocks = n_img_blocks, n_ref_blocks
@@ -360,6 +366,7 @@ def make_stack_desc(n_img: int, n_txt: int, n_img_blocks: int, n_txt_blocks: int
     d.width, d.n_heads, d.head_dim, d.mlp_hidden = width, n_heads, head_dim, mlp_hidden
     d.rope_theta, d.ln_eps, d.qk_eps = configs.ROPE_THETA, configs.LN_EPS, configs.QK_EPS
     d.cfg_scale = cfg_scale
+    d.flags = DIT_STACK_TEXT_SIDE_STREAM if side_stream else 0
     return d
 
 

@@ -284,7 +284,19 @@ typedef struct dit_stack_desc {
   float qk_eps;           /* 1e-6                                                  */
   float cfg_scale;        /* guidance scale, finite; 1 runs the conditional branch */
                           /* only (no negative forward)                           */
+  uint32_t flags;         /* DIT_STACK_* bits, 0 for none                          */
 } dit_stack_desc;
+
+/* Run the stage-1 text blocks of both branches on a second stream, beside
+ * the stage-1 image and reference blocks (they read no image rows: "Welcome
+ * FLUX.3 Image Klein in Diffusers", "How it works", the stage-1 streams are
+ * processed separately).  The library owns that stream (one per device,
+ * created on first use, non-blocking, default priority) and joins it back
+ * into the caller's stream with events before the joint blocks, so the call
+ * stays asynchronous and capturable in a HIP graph.  Costs a second block
+ * workspace at n_txt tokens (counted by dit_stack_workspace_bytes).  Results
+ * are bitwise those of the serial order. */
+#define DIT_STACK_TEXT_SIDE_STREAM 1u
 
 /* Device pointers of one block's parameters. */
 typedef struct dit_block_params {
@@ -299,7 +311,8 @@ typedef struct dit_block_params {
 
 /* Bytes of device workspace dit_stack_fwd needs: the block workspace at
  * N = n_img + n_ref + n_txt plus two [N, D] bf16 activation buffers (one per
- * branch). */
+ * branch), plus a block workspace at n_txt tokens with
+ * DIT_STACK_TEXT_SIDE_STREAM. */
 int dit_stack_workspace_bytes(const dit_stack_desc* desc, size_t* bytes);
 
 /* One guided stack forward.
@@ -351,7 +364,9 @@ int dit_stack_fwd(const dit_stack_desc* desc, const void* x_img, const void* x_r
 #define DIT_TIME_DIM 256
 
 typedef struct dit_model_desc {
-  dit_stack_desc stack; /* tokens, block counts, widths, eps and cfg_scale          */
+  dit_stack_desc stack; /* tokens, block counts, widths, eps and cfg_scale; its     */
+                        /* flags must be 0 (the text blocks run once, in           */
+                        /* dit_sampler_prepare)                                    */
   int32_t latent_ch;    /* C, channels of a latent token (128): a multiple of 32,   */
                         /* at most 8192                                             */
   int32_t text_dim;     /* width of a text feature (20480): a multiple of 16        */

@@ -210,7 +210,7 @@ def stack_ws(lib, d):
 
 
 def test_stack_struct_layout():
-    assert ctypes.sizeof(ops.StackDesc) == 60
+    assert ctypes.sizeof(ops.StackDesc) == 64
     assert ctypes.sizeof(ops.BlockParams) == 40
 
 
@@ -227,6 +227,11 @@ def test_stack_workspace_bytes(lib):
                                               n_ref_blocks=5))
     rc_b, nb = ws(lib, ops.make_desc([4096, 4096, 160]))
     assert rc == OK and n == nb + 2 * 8352 * 3072 * 2
+    # the side stream's text blocks take a block workspace of their own
+    rc, n_side = stack_ws(lib, ops.make_stack_desc(4096, 160, 5, 5, 28, 4.0, side_stream=True))
+    rc_b, nb = ws(lib, ops.make_desc([4096, 160]))
+    rc_t, nt = ws(lib, ops.make_desc([160]))
+    assert rc == OK and n_side == nb + 2 * 4256 * 3072 * 2 + nt
 
 
 @pytest.mark.parametrize("field,value,want", [
@@ -234,7 +239,8 @@ def test_stack_workspace_bytes(lib):
     ("n_joint_blocks", 2000, SHAPE), ("width", 3000, SHAPE), ("head_dim", 64, SHAPE),
     ("cfg_scale", float("nan"), ARG), ("qk_eps", -1.0, ARG), ("n_ref", -1, SHAPE),
     ("n_ref_blocks", 1, SHAPE),  # reference blocks without reference tokens
-    ("n_ref", 131072, SHAPE)])  # the joint sequence above DIT_MAX_TOKENS
+    ("n_ref", 131072, SHAPE),  # the joint sequence above DIT_MAX_TOKENS
+    ("flags", 2, ARG)])  # an unknown flag bit
 def test_stack_desc_validation(lib, field, value, want):
     d = ops.make_stack_desc(256, 80, 1, 1, 2, 4.0)
     setattr(d, field, value)
@@ -286,7 +292,7 @@ def test_stack_fwd_host_errors(lib):
 # ---- sampler ---------------------------------------------------------------------
 
 def test_sampler_struct_layout():
-    assert ctypes.sizeof(ops.ModelDesc) == 68
+    assert ctypes.sizeof(ops.ModelDesc) == 72
     assert ctypes.sizeof(ops.BlockWeights) == 32
     assert ctypes.sizeof(ops.ModelWeights) == 23 * 8
 
@@ -411,6 +417,10 @@ def test_sampler_host_errors(lib):
     assert step_call(lib, d, w, z=0) == NULL
     assert step_call(lib, d, w, sigma=float("inf")) == ARG
     assert step_call(lib, d, w, ws_bytes=small) == WS
+    # the sampler's text blocks run once, in prepare: no side-stream flag
+    ds = model_desc()
+    ds.stack.flags = ops.DIT_STACK_TEXT_SIDE_STREAM
+    assert sampler_ws(lib, ds)[0] == ARG
     assert step_call(lib, d, w, z=P + (4 << 30)) == ARG     # latent inside the workspace
     assert step_call(lib, d, w, v=P) == ARG                 # velocity over the latent
     assert step_call(lib, d, w, v=BAD) == ALIGN

@@ -151,3 +151,61 @@ def test_stack_full_depth_parity(scale):
     tol = tol_full_depth(n_t + n_j, scale)
     log(f"  relL2 {e:.3e} (bound {tol:.3e})")
     assert e <= tol
+
+
+def dev_stack_args(x_img, x_c, x_n, pos, blocks):
+    return (ops.to_device_bf16(x_img), ops.to_device_bf16(x_c), ops.to_device_bf16(x_n),
+            torch.from_numpy(pos).cuda(), to_dev_blocks(blocks))
+
+
+def test_stack_side_stream_matches_serial():
+    # DIT_STACK_TEXT_SIDE_STREAM runs the stage-1 text blocks of both branches
+    # on the library's second stream, beside the image blocks: the same
+    # kernels on the same rows, so the result is bitwise the serial one
+    require_gpu()
+    n_i, n_t, n_j = 2, 2, 2
+    x_img, x_c, x_n, pos, blocks = stack_inputs(16, 80, n_i, n_t, n_j, seed=10)
+    xi, xc, xn, p, bl = dev_stack_args(x_img, x_c, x_n, pos, blocks)
+    out = []
+    for side in (False, True):
+        desc = ops.make_stack_desc(256, 80, n_i, n_t, n_j, 4.0, side_stream=side)
+        log(f"stack 256 img + 80 txt, blocks {n_i}+{n_t}+{n_j}, side stream {side}")
+        v = torch.full((256, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        ops.stack_fwd(desc, xi, xc, xn, p, bl, v_img=v)
+        torch.cuda.synchronize()
+        out.append(v.cpu())
+    assert torch.equal(out[0], out[1])
+
+
+@pytest.mark.parametrize("side", [False, True])
+def test_stack_graph_replays_match_eager(side):
+    # The guided stack captured in a HIP graph through torch's capture of the
+    # caller's stream (with the side stream, its fork and join events bring
+    # it into the capture), replayed three times with eager launches and
+    # synchronizations between the replays and a poisoned output before
+    # each: every replay equals the eager result bitwise.
+    require_gpu()
+    n_i, n_t, n_j = 1, 1, 2
+    x_img, x_c, x_n, pos, blocks = stack_inputs(8, 80, n_i, n_t, n_j, seed=11)
+    xi, xc, xn, p, bl = dev_stack_args(x_img, x_c, x_n, pos, blocks)
+    desc = ops.make_stack_desc(64, 80, n_i, n_t, n_j, 4.0, side_stream=side)
+    ws = torch.empty(ops.stack_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    v_e = torch.empty((64, D), dtype=torch.bfloat16, device="cuda")
+    v_g = torch.empty_like(v_e)
+    log(f"stack graph, side stream {side}")
+    ops.stack_fwd(desc, xi, xc, xn, p, bl, v_img=v_e, workspace=ws)
+    torch.cuda.synchronize()
+    want = v_e.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.stack_fwd(desc, xi, xc, xn, p, bl, v_img=v_g, workspace=ws)
+    for r in range(3):
+        v_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(v_g, want), f"replay {r}"
+        # eager work between replays, on the same workspace
+        ops.stack_fwd(desc, xi, xc, xn, p, bl, v_img=v_e, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(v_e, want), f"eager after replay {r}"

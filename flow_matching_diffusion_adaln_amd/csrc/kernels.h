@@ -84,7 +84,7 @@ hipError_t launch_gemm_out(const uint16_t* cat, const uint16_t* w_out, int M, in
 // (thin_partial_bytes) are summed by the last piece to arrive, counted in
 // `counters` (D / 128 ints, zero at launch, left zero); with too little
 // scratch it runs whole columns instead.
-constexpr int kThinMaxTokens = 128;
+constexpr int kThinMaxTokens = 160;
 constexpr int kThinMaxPieces = 32;
 bool thin_fits(int M, int D, int F);
 size_t thin_partial_bytes(int M, int D, int pieces);

@@ -1,4 +1,4 @@
-// Input and output projections of short sequences (at most 128 tokens).
+// Input and output projections of short sequences (at most 160 tokens).
 //
 // The text-only stage-1 blocks run on prompts of 80-token multiples ("Welcome
 // FLUX.3 Image Klein in Diffusers", "How it works"): at that length a
@@ -10,7 +10,7 @@
 // range (input projection) or one K piece (output projection, whose 24 column
 // blocks are too few to keep the CUs streaming).  Its four waves own 32 rows
 // each and share the activation tile; every token of the sequence sits in
-// the MFMAs' other operand (up to 4 blocks of 32).  The loads go straight to
+// the MFMAs' other operand (up to 5 blocks of 32).  The loads go straight to
 // LDS through a 4-stage ring.  The epilogues run in the same kernel:
 //  * input projection: a 128-row block is one q or k head (per-head RMSNorm
 //    with the learnable scale, then the 4-axis RoPE, 32 dims per axis: the
@@ -129,7 +129,8 @@ __global__ __launch_bounds__(256, 1) void thin_kernel(ThinArgs g) {
   // fixed bounds (not MB): an array of template-dependent type would make
   // the direct-load builtins dependent, and the host pass would then drop the
   // kernel's host stub
-  uint32_t woff[4], aoff[4];
+  uint32_t woff[4], aoff[8];
+  static_assert(MB <= 8, "activation load offsets");
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = (4 * wave + j) * 8 + lrow;
@@ -382,7 +383,8 @@ hipError_t launch_thin(const ThinArgs& g, hipStream_t stream) {
     case 1: hipLaunchKernelGGL((thin_kernel<EPI, 1>), grid, block, 0, stream, g); break;
     case 2: hipLaunchKernelGGL((thin_kernel<EPI, 2>), grid, block, 0, stream, g); break;
     case 3: hipLaunchKernelGGL((thin_kernel<EPI, 3>), grid, block, 0, stream, g); break;
-    default: hipLaunchKernelGGL((thin_kernel<EPI, 4>), grid, block, 0, stream, g); break;
+    case 4: hipLaunchKernelGGL((thin_kernel<EPI, 4>), grid, block, 0, stream, g); break;
+    default: hipLaunchKernelGGL((thin_kernel<EPI, 5>), grid, block, 0, stream, g); break;
   }
   return hipGetLastError();
 }

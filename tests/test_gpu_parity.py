@@ -240,12 +240,13 @@ def test_block_parity_single_token():
     check_block(block_config("one", (1,), 92))
 
 
-# At most 128 tokens the projections stream their weights: a workgroup per
+# At most 160 tokens the projections stream their weights: a workgroup per
 # 128 weight rows with every token in the other MFMA operand (4 blocks of 32
-# at 128 tokens, a last block only partly inside M at 97), the output
-# projection's K cut into pieces merged by the last to arrive, and two
-# streams (100 image + 28 text) for the per-stream gate.
-@pytest.mark.parametrize("n_tokens,cid", [((128,), 97), ((97,), 98), ((100, 28), 99)])
+# at 128 tokens, 5 at 160, a last block only partly inside M at 97 and 129),
+# the output projection's K cut into pieces merged by the last to arrive, and
+# two streams (100 image + 28 text) for the per-stream gate.
+@pytest.mark.parametrize("n_tokens,cid", [((128,), 97), ((97,), 98), ((100, 28), 99),
+                                          ((160,), 104), ((129,), 105)])
 def test_block_parity_short_128_row_tiles(n_tokens, cid):
     check_block(block_config(f"short{sum(n_tokens)}", n_tokens, cid))
 

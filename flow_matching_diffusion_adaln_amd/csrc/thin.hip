@@ -26,7 +26,6 @@
 namespace dit {
 namespace {
 
-constexpr int TBN = 128;  // weight rows per workgroup (4 waves x 32)
 constexpr int TBK = 64;   // k per LDS tile: rows of 128 bytes
 constexpr int TNS = 4;    // ring stages
 constexpr int kScopeDevice = 16;  // cache-policy bits of device-scope (sc1) buffer accesses
@@ -76,28 +75,33 @@ __device__ __forceinline__ uint2 pack4f(float a, float b, float c, float d) {
   return make_uint2(pack2(a, b), pack2(c, d));
 }
 
-// weight row feeding row r (0..127) of column block cb
-template <int EPI>
+// weight row feeding row r of column block cb (BNW rows per block)
+template <int EPI, int BNW>
 __device__ __forceinline__ int thin_weight_row(const ThinArgs& g, int cb, int r) {
   if (EPI == TH_IN) {
     const int n_qkv = 3 * g.H;
-    if (cb < n_qkv) return cb * TBN + r;
+    if (cb < n_qkv) return cb * BNW + r;
     // 64 hidden units: wave w's 32 rows are 16 gate rows, then the up rows
     // of the same 16 units
     const int w = r >> 5, i = r & 31;
     return 3 * g.D + (i >= 16 ? g.F : 0) + (cb - n_qkv) * 64 + 16 * w + (i & 15);
   }
-  return cb * TBN + r;
+  return cb * BNW + r;
 }
 
-template <int EPI, int MB>
-__global__ __launch_bounds__(256, 1) void thin_kernel(ThinArgs g) {
+// NWV waves of 32 weight rows each: 4 (128 rows, a whole head) for the input
+// projection, 2 for the output projection, whose last-arriving piece then
+// sums half as many partial rows.
+template <int EPI, int MB, int NWV>
+__global__ __launch_bounds__(64 * NWV, 1) void thin_kernel(ThinArgs g) {
+  constexpr int BNW = 32 * NWV;  // weight rows per workgroup
+  static_assert(EPI == TH_OUT || NWV == 4, "a q / k block is one 128-dim head");
   // one LDS array per stage (see the big GEMM: the compiler then knows the
   // fragment reads of one stage do not alias the loads into the others)
-  __shared__ __attribute__((aligned(16))) uint16_t s_w0[TBN * TBK];
-  __shared__ __attribute__((aligned(16))) uint16_t s_w1[TBN * TBK];
-  __shared__ __attribute__((aligned(16))) uint16_t s_w2[TBN * TBK];
-  __shared__ __attribute__((aligned(16))) uint16_t s_w3[TBN * TBK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w0[BNW * TBK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w1[BNW * TBK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w2[BNW * TBK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w3[BNW * TBK];
   __shared__ __attribute__((aligned(16))) uint16_t s_a0[MB * 32 * TBK];
   __shared__ __attribute__((aligned(16))) uint16_t s_a1[MB * 32 * TBK];
   __shared__ __attribute__((aligned(16))) uint16_t s_a2[MB * 32 * TBK];
@@ -129,16 +133,18 @@ __global__ __launch_bounds__(256, 1) void thin_kernel(ThinArgs g) {
   // fixed bounds (not MB): an array of template-dependent type would make
   // the direct-load builtins dependent, and the host pass would then drop the
   // kernel's host stub
-  uint32_t woff[4], aoff[8];
-  static_assert(MB <= 8, "activation load offsets");
+  constexpr int AJ = 4 * MB / NWV;  // activation slabs per wave
+  uint32_t woff[4], aoff[16];
+  static_assert(AJ * NWV == 4 * MB && AJ <= 16, "activation load offsets");
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = (4 * wave + j) * 8 + lrow;
-    woff[j] = (uint32_t)thin_weight_row<EPI>(g, cb, r) * rowb + (uint32_t)((lch ^ tswz(r)) * 16);
+    woff[j] = (uint32_t)thin_weight_row<EPI, BNW>(g, cb, r) * rowb +
+              (uint32_t)((lch ^ tswz(r)) * 16);
   }
 #pragma unroll
-  for (int j = 0; j < MB; ++j) {
-    const int r = (MB * wave + j) * 8 + lrow;
+  for (int j = 0; j < AJ; ++j) {
+    const int r = (AJ * wave + j) * 8 + lrow;
     aoff[j] = (uint32_t)min(r, g.M - 1) * rowb + (uint32_t)((lch ^ tswz(r)) * 16);
   }
   const char* wbase = reinterpret_cast<const char*>(g.W);
@@ -152,11 +158,11 @@ __global__ __launch_bounds__(256, 1) void thin_kernel(ThinArgs g) {
       __builtin_amdgcn_global_load_lds(wbase + (woff[j] + ko),
                                        (lds_ptr)(ring_w[st] + (4 * wave + j) * 8 * TBK), 16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < MB; ++j)
+    for (int j = 0; j < AJ; ++j)
       __builtin_amdgcn_global_load_lds(abase + (aoff[j] + ko),
-                                       (lds_ptr)(ring_a[st] + (MB * wave + j) * 8 * TBK), 16, 0, 0);
+                                       (lds_ptr)(ring_a[st] + (AJ * wave + j) * 8 * TBK), 16, 0, 0);
   };
-  constexpr int NLD = 4 + MB;  // loads per wave per stage
+  constexpr int NLD = 4 + AJ;  // loads per wave per stage
   // s_waitcnt with vmcnt(n) only (expcnt, lgkmcnt left alone)
   constexpr int VM_WAIT = ((TNS - 2) * NLD & 15) | (((TNS - 2) * NLD >> 4) << 14) | 0x0F70;
 
@@ -293,9 +299,9 @@ __global__ __launch_bounds__(256, 1) void thin_kernel(ThinArgs g) {
       // point, and every wave's stores complete before the barrier that
       // precedes the count.
       const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          g.partial, 0, (int)((size_t)g.n_cb * g.pieces * 4 * MB * 4 * 64 * 16), 0x00020000);
+          g.partial, 0, (int)((size_t)g.n_cb * g.pieces * NWV * MB * 4 * 64 * 16), 0x00020000);
       auto goff = [&](int slot, int i, int rr) __attribute__((always_inline)) {
-        return (int)(((((slot * 4 + wave) * MB + i) * 4 + rr) * 64 + lane) * 16);
+        return (int)(((((slot * NWV + wave) * MB + i) * 4 + rr) * 64 + lane) * 16);
       };
 #pragma unroll
       for (int i = 0; i < MB; ++i)
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(256, 1) void thin_kernel(ThinArgs g) {
     }
     // y = x + gate_s r (flags: bit 0 no residual, bit 1 no gate)
     const bool use_gate = !(g.flags & 2u), use_res = !(g.flags & 1u);
-    const int c0 = cb * TBN + 32 * wave + 4 * hl;
+    const int c0 = cb * BNW + 32 * wave + 4 * hl;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int t = 32 * i + ln;
@@ -376,18 +382,21 @@ __global__ __launch_bounds__(256, 1) void thin_kernel(ThinArgs g) {
   }
 }
 
-template <int EPI>
+template <int EPI, int NWV>
 hipError_t launch_thin(const ThinArgs& g, hipStream_t stream) {
-  const dim3 grid(g.n_cb * g.pieces), block(256);
+  const dim3 grid(g.n_cb * g.pieces), block(64 * NWV);
   switch ((g.M + 31) / 32) {
-    case 1: hipLaunchKernelGGL((thin_kernel<EPI, 1>), grid, block, 0, stream, g); break;
-    case 2: hipLaunchKernelGGL((thin_kernel<EPI, 2>), grid, block, 0, stream, g); break;
-    case 3: hipLaunchKernelGGL((thin_kernel<EPI, 3>), grid, block, 0, stream, g); break;
-    case 4: hipLaunchKernelGGL((thin_kernel<EPI, 4>), grid, block, 0, stream, g); break;
-    default: hipLaunchKernelGGL((thin_kernel<EPI, 5>), grid, block, 0, stream, g); break;
+    case 1: hipLaunchKernelGGL((thin_kernel<EPI, 1, NWV>), grid, block, 0, stream, g); break;
+    case 2: hipLaunchKernelGGL((thin_kernel<EPI, 2, NWV>), grid, block, 0, stream, g); break;
+    case 3: hipLaunchKernelGGL((thin_kernel<EPI, 3, NWV>), grid, block, 0, stream, g); break;
+    case 4: hipLaunchKernelGGL((thin_kernel<EPI, 4, NWV>), grid, block, 0, stream, g); break;
+    default: hipLaunchKernelGGL((thin_kernel<EPI, 5, NWV>), grid, block, 0, stream, g); break;
   }
   return hipGetLastError();
 }
+
+// Rows per workgroup of the output projection (2 waves of 32).
+constexpr int kOutRows = 64;
 
 }  // namespace
 
@@ -397,7 +406,8 @@ bool thin_fits(int M, int D, int F) {
 }
 
 size_t thin_partial_bytes(int M, int D, int pieces) {
-  return (size_t)(D / TBN) * pieces * 4 * ((M + 31) / 32) * 4 * 64 * 16;
+  // per piece and 32 output columns: a wave's 4 KB groups for each token block
+  return (size_t)(D / 32) * pieces * ((M + 31) / 32) * 4 * 64 * 16;
 }
 
 hipError_t launch_thin_in(const uint16_t* u, const uint16_t* w_in, int M, int D, int F,
@@ -426,11 +436,11 @@ hipError_t launch_thin_in(const uint16_t* u, const uint16_t* w_in, int M, int D,
   g.q_mul = q_mul;
   const double two_pi = 6.283185307179586;
   for (int j = 0; j < 16; ++j) g.rope_rev[j] = pow((double)theta, -2.0 * j / 32.0) / two_pi;
-  return launch_thin<TH_IN>(g, stream);
+  return launch_thin<TH_IN, 4>(g, stream);
 }
 
 int thin_out_pieces(int D, int F) {
-  const int n_cb = D / TBN, units = (D + F) / (TBK * TNS);
+  const int n_cb = D / kOutRows, units = (D + F) / (TBK * TNS);
   // one round of workgroups (a second round would repeat the whole stream time)
   int p = device_cus() / n_cb;
   if (p > units) p = units;
@@ -451,7 +461,7 @@ hipError_t launch_thin_out(const uint16_t* cat, const uint16_t* w_out, int M, in
   g.D = D;
   g.F = F;
   g.H = D / 128;
-  g.n_cb = D / TBN;
+  g.n_cb = D / kOutRows;
   g.pieces = thin_out_pieces(D, F);
   while (g.pieces > 1 &&
          (thin_partial_bytes(M, D, g.pieces) > partial_bytes || g.n_cb > n_counters))
@@ -464,7 +474,7 @@ hipError_t launch_thin_out(const uint16_t* cat, const uint16_t* w_out, int M, in
   g.flags = flags;
   g.partial = partial;
   g.counters = counters;
-  return launch_thin<TH_OUT>(g, stream);
+  return launch_thin<TH_OUT, kOutRows / 32>(g, stream);
 }
 
 }  // namespace dit

@@ -370,9 +370,13 @@ int check_stack(const dit_stack_desc* d, Shape* joint, size_t* bytes) {
 
 // The side stream of DIT_STACK_TEXT_SIDE_STREAM and its fork / join events,
 // one set per device, created on first use and kept until the process ends.
+// A call holds `use` from recording the fork to enqueuing the wait on the
+// join, so calls from several host threads cannot re-record the shared
+// events between another call's record and wait.
 struct SideStream {
   hipStream_t stream;
   hipEvent_t fork, join;
+  std::mutex* use;
 };
 std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
@@ -394,6 +398,7 @@ const SideStream* side_stream(int* rc) {
       *rc = DIT_ERR_HIP;
       return nullptr;
     }
+    s.use = new std::mutex();  // kept until the process ends, like the stream
     g_side[dev] = s;
     g_side_ok[dev] = true;
   }
@@ -818,6 +823,7 @@ int dit_stack_fwd(const dit_stack_desc* desc, const void* x_img, const void* x_r
     // the joint blocks wait for the join.
     const SideStream* side = side_stream(&rc);
     if (!side) return rc;
+    std::lock_guard<std::mutex> lock(*side->use);
     Shape ts = js;
     ts.N = desc->n_txt;
     char* wst = xn + act;

@@ -25,9 +25,11 @@
  *   - Tensors are device pointers owned by the caller, row-major, bf16 stored
  *     as 16-bit patterns unless stated.  They must be 16-byte aligned.
  *   - Work is enqueued on `stream` (0 = the null stream); calls return once
- *     enqueued.  The library never allocates, frees or synchronizes; its only
- *     global state is a per-device cache of the CU count, so calls may come
- *     from several threads.
+ *     enqueued.  The library never allocates or frees device memory and
+ *     never synchronizes with the host.  Its global state, per device: a
+ *     cache of the CU count, the scratch array of dit_block_fwd_noalloc, and
+ *     the side stream of DIT_STACK_TEXT_SIDE_STREAM with its events (created
+ *     on first use); calls may come from several threads.
  *   - Validation runs on the host before any launch; on error nothing is
  *     launched and outputs are untouched.  Errors are negative status codes,
  *     and dit_status_str() names them.
@@ -293,7 +295,8 @@ typedef struct dit_stack_desc {
  * processed separately).  The library owns that stream (one per device,
  * created on first use, non-blocking, default priority) and joins it back
  * into the caller's stream with events before the joint blocks, so the call
- * stays asynchronous and capturable in a HIP graph.  Costs a second block
+ * stays asynchronous and capturable in a HIP graph.  All calls on a device
+ * share that stream, so their text blocks run one call after another.  Costs a second block
  * workspace at n_txt tokens (counted by dit_stack_workspace_bytes).  Results
  * are bitwise those of the serial order. */
 #define DIT_STACK_TEXT_SIDE_STREAM 1u

@@ -986,9 +986,10 @@ namespace {
 // run in rounds of `cus`.  A last round holding only a few tiles would leave
 // most CUs idle for a whole tile time, so when at least one full round exists
 // and the last round is at most half full, its tail tiles are cut along K
-// into pieces of whole 4-k-tile units, one piece per CU (or per unit when
-// there are fewer units than CUs); the fix-up kernel then sums each tile's
-// fp32 partials in K order and runs the epilogue.
+// into pieces of whole units (the K loop's unroll period of 6 or 2 k tiles),
+// one piece per CU (or per unit when there are fewer units than CUs); the
+// fix-up kernel then sums each tile's fp32 partials in K order and runs the
+// epilogue.
 // K loop unroll period in k tiles: 6 (3 A slots) when it divides K / BK,
 // else 2 (K is a multiple of 128 for every supported shape).
 int unroll_period(int KT) { return KT % 6 == 0 ? 6 : 2; }
@@ -1041,8 +1042,9 @@ Plan make_plan(int bm, int M, int KT, int num_n, bool can_split) {
 // hold q or k tiles: the fix-up's epilogue does not normalize or rotate.
 //
 // 128-row tiles (1 x 4 waves of 128 x 64) serve sequences of at most 128
-// tokens when every tile is split (an 80-token text block: one row of tiles,
-// where a 224-row tile would run 2.8 times the MFMAs the 80 rows need).
+// tokens when every tile is split and the weight-streaming kernels of
+// thin.hip do not take the shape (an 80-token block: one row of tiles, where
+// a 224-row tile would run 2.8 times the MFMAs the 80 rows need).
 // Their whole-tile epilogues are then never used; bf16 only.  For longer
 // sequences they were measured slower than 224-row tiles (336 tokens, output
 // projection: more tiles with the same fixed costs each).

@@ -7,9 +7,9 @@
 // so it is bound by reading each weight byte once from HBM, not by the MFMAs.
 //
 // A workgroup owns 128 weight rows (output columns) and runs its whole K
-// range (input projection) or one K piece (output projection, whose 24 column
-// blocks are too few to keep the CUs streaming).  Its four waves own 32 rows
-// each and share the activation tile; every token of the sequence sits in
+// range (input projection), or 64 rows and one K piece (output projection,
+// whose 48 column blocks are too few to keep the CUs streaming).  Its waves
+// own 32 rows each and share the activation tile; every token of the sequence sits in
 // the MFMAs' other operand (up to 5 blocks of 32).  The loads go straight to
 // LDS through a 4-stage ring.  The epilogues run in the same kernel:
 //  * input projection: a 128-row block is one q or k head (per-head RMSNorm
@@ -39,7 +39,7 @@ struct ThinArgs {
   const uint16_t* W;  // weights, rows of K
   int M, K, KT;       // KT = K / 64, a multiple of TNS
   int D, F, H;
-  int n_cb;           // column blocks of 128 weight rows
+  int n_cb;           // column blocks (128 weight rows in, 64 out)
   int pieces;         // K pieces per column block
   // input projection
   uint16_t* q;

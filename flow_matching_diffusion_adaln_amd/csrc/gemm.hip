@@ -74,7 +74,10 @@ struct GemmArgs {
   float qk_eps;
   float theta;
   float q_mul;             // multiplies the normalized, rotated q before it is stored
-  double rope_rev[16];     // theta^(-2j / 32) / (2 pi): turns per position step of pair j
+  // theta^(-2j / 32) / (2 pi), the turns per position step of pair j, as
+  // hi + lo: hi keeps 8 significant bits, so pos * hi is exact in fp32 for
+  // |pos| < 2^16 and the turn count's fraction costs no fp64 work
+  float rope_hi[16], rope_lo[16];
   // output projection
   const uint16_t* x;  // residual [M, D]
   const uint16_t* mod;  // [S, 3, D]
@@ -261,6 +264,15 @@ __device__ __forceinline__ void store_staged(const char* st, int n_rows, uint16_
   }
 }
 
+// Fraction of pos * (hi + lo) turns: pos * hi is exact (hi has 8
+// significant bits, |pos| < 2^16), so its fraction is exact too, and one fma
+// adds pos * lo before the second reduction; the result is within about 2^-24
+// (|pos lo| + 1) of the exact fraction.
+__device__ __forceinline__ float turn_fraction(float pos, float hi, float lo) {
+  const float a = __builtin_amdgcn_fractf(pos * hi);
+  return __builtin_amdgcn_fractf(fmaf(pos, lo, a));
+}
+
 // q / k tile epilogue of the 256-row layout: per-head RMSNorm with the
 // learnable scale, then 4-axis RoPE, straight from the fp32 accumulators
 // (the same operations the standalone rope4 kernel applies to stored q, k).
@@ -287,13 +299,13 @@ __device__ __forceinline__ void epilogue_qk(const GemmArgs& g, const f32x16 (&ac
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
       gsc[j][rr] = *reinterpret_cast<const uint2*>(scale + j * 32 + 8 * rr + 4 * hl);
-  double fr[4][2];
+  float fh[4][2], fl[4][2];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
-      const double f0 = g.rope_rev[4 * rr + pr], f1 = g.rope_rev[4 * rr + 2 + pr];
-      fr[rr][pr] = hl ? f1 : f0;
+      fh[rr][pr] = hl ? g.rope_hi[4 * rr + 2 + pr] : g.rope_hi[4 * rr + pr];
+      fl[rr][pr] = hl ? g.rope_lo[4 * rr + 2 + pr] : g.rope_lo[4 * rr + pr];
     }
   int4 p4[MB];
 #pragma unroll
@@ -315,7 +327,10 @@ __device__ __forceinline__ void epilogue_qk(const GemmArgs& g, const f32x16 (&ac
     const int pa[4] = {p4[i].x, p4[i].y, p4[i].z, p4[i].w};
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const double pj = (double)pa[j];
+      const float pj = (float)pa[j];
+      // position 0 on this axis in every lane of the wave (t and l of image
+      // tokens, h, w and l of text tokens): nothing turns, no angles needed
+      const bool turn = __ballot(pa[j] != 0) != 0;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const uint2 gs = gsc[j][rr];
@@ -323,16 +338,17 @@ __device__ __forceinline__ void epilogue_qk(const GemmArgs& g, const f32x16 (&ac
                             acc[i][j][4 * rr + 1] * rstd * hi2f(gs.x),
                             acc[i][j][4 * rr + 2] * rstd * lo2f(gs.y),
                             acc[i][j][4 * rr + 3] * rstd * hi2f(gs.y)};
-        float y[4];
+        float y[4] = {x[0], x[1], x[2], x[3]};
+        if (turn) {
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          // pair 4 rr + 2 hl + pr of axis j; the turn count is reduced to
-          // [0, 1) in double, then sin / cos of 2 pi r in hardware
-          const double t = pj * fr[rr][pr];
-          const float r = (float)(t - floor(t));
-          const float sn = __builtin_amdgcn_sinf(r), cs = __builtin_amdgcn_cosf(r);
-          y[2 * pr] = x[2 * pr] * cs - x[2 * pr + 1] * sn;
-          y[2 * pr + 1] = x[2 * pr] * sn + x[2 * pr + 1] * cs;
+          for (int pr = 0; pr < 2; ++pr) {
+            // pair 4 rr + 2 hl + pr of axis j: the turn count reduced to
+            // [0, 1), then sin / cos of 2 pi r in hardware
+            const float r = turn_fraction(pj, fh[rr][pr], fl[rr][pr]);
+            const float sn = __builtin_amdgcn_sinf(r), cs = __builtin_amdgcn_cosf(r);
+            y[2 * pr] = x[2 * pr] * cs - x[2 * pr + 1] * sn;
+            y[2 * pr + 1] = x[2 * pr] * sn + x[2 * pr + 1] * cs;
+          }
         }
         // staged at row i 32 + ln, columns j 32 + 8 rr + 4 hl .. + 3
         *reinterpret_cast<uint2*>(st + st_off<16>(i * 32 + ln, 4 * j + rr) + 8 * hl) =
@@ -367,13 +383,13 @@ __device__ __forceinline__ void epilogue_qk224(const GemmArgs& g,
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
       gsc[j][rr] = *reinterpret_cast<const uint2*>(scale + (2 * hh + j) * 32 + 8 * rr + 4 * hl);
-  double fr[4][2];
+  float fh[4][2], fl[4][2];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
-      const double f0 = g.rope_rev[4 * rr + pr], f1 = g.rope_rev[4 * rr + 2 + pr];
-      fr[rr][pr] = hl ? f1 : f0;
+      fh[rr][pr] = hl ? g.rope_hi[4 * rr + 2 + pr] : g.rope_hi[4 * rr + pr];
+      fl[rr][pr] = hl ? g.rope_lo[4 * rr + 2 + pr] : g.rope_lo[4 * rr + pr];
     }
   int4 p4[MB];
 #pragma unroll
@@ -402,7 +418,8 @@ __device__ __forceinline__ void epilogue_qk224(const GemmArgs& g,
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int pax = hh ? (j ? p4[i].w : p4[i].z) : (j ? p4[i].y : p4[i].x);
-      const double pj = (double)pax;
+      const float pj = (float)pax;
+      const bool turn = __ballot(pax != 0) != 0;  // as in epilogue_qk
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const uint2 gs = gsc[j][rr];
@@ -410,14 +427,15 @@ __device__ __forceinline__ void epilogue_qk224(const GemmArgs& g,
                             acc[i][j][4 * rr + 1] * rstd * hi2f(gs.x),
                             acc[i][j][4 * rr + 2] * rstd * lo2f(gs.y),
                             acc[i][j][4 * rr + 3] * rstd * hi2f(gs.y)};
-        float y[4];
+        float y[4] = {x[0], x[1], x[2], x[3]};
+        if (turn) {
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const double t = pj * fr[rr][pr];
-          const float r = (float)(t - floor(t));
-          const float sn = __builtin_amdgcn_sinf(r), cs = __builtin_amdgcn_cosf(r);
-          y[2 * pr] = x[2 * pr] * cs - x[2 * pr + 1] * sn;
-          y[2 * pr + 1] = x[2 * pr] * sn + x[2 * pr + 1] * cs;
+          for (int pr = 0; pr < 2; ++pr) {
+            const float r = turn_fraction(pj, fh[rr][pr], fl[rr][pr]);
+            const float sn = __builtin_amdgcn_sinf(r), cs = __builtin_amdgcn_cosf(r);
+            y[2 * pr] = x[2 * pr] * cs - x[2 * pr + 1] * sn;
+            y[2 * pr + 1] = x[2 * pr] * sn + x[2 * pr + 1] * cs;
+          }
         }
         // staged at row i 32 + ln, columns j 32 + 8 rr + 4 hl .. + 3
         *reinterpret_cast<uint2*>(st + st_off<8>(i * 32 + ln, 4 * j + rr) + 8 * hl) =
@@ -1139,7 +1157,14 @@ GemmArgs in_args(const void* u, const void* w_in, int M, int D, int F, uint16_t*
   g.q_mul = 1.0f;
   g.theta = theta;
   const double two_pi = 6.283185307179586;
-  for (int j = 0; j < 16; ++j) g.rope_rev[j] = pow((double)theta, -2.0 * j / 32.0) / two_pi;
+  for (int j = 0; j < 16; ++j) {
+    const double rev = pow((double)theta, -2.0 * j / 32.0) / two_pi;
+    int e;
+    frexp(rev, &e);  // rev = m 2^e, 0.5 <= m < 1
+    const double hi = ldexp(nearbyint(ldexp(rev, 8 - e)), e - 8);
+    g.rope_hi[j] = (float)hi;  // exact: 8 significant bits
+    g.rope_lo[j] = (float)(rev - hi);
+  }
   g.partial = partial;
   g.A = static_cast<const uint16_t*>(u);
   g.W = static_cast<const uint16_t*>(w_in);

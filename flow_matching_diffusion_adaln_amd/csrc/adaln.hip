@@ -38,6 +38,18 @@ __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t* __restrict__
   uint4 v[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) v[i] = xr[lane + 64 * i];
+  // the stream's shift and scale are loaded with x, before the statistics,
+  // so the wave waits for memory once rather than once per chunk
+  const int st = stream_of(row, e0, e1);
+  const uint4* shift = reinterpret_cast<const uint4*>(mod + (size_t)st * 3 * W);
+  const uint4* scale = reinterpret_cast<const uint4*>(mod + (size_t)st * 3 * W + W);
+  uint4 shv[CPL], scv[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    shv[i] = shift[lane + 64 * i];
+    scv[i] = scale[lane + 64 * i];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the loads above the statistics
 
   float s = 0.f;
 #pragma unroll
@@ -59,14 +71,11 @@ __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t* __restrict__
   }
   const float rstd = rsqrtf(wave_sum(ss) * (1.0f / W) + eps);
 
-  const int st = stream_of(row, e0, e1);
-  const uint4* shift = reinterpret_cast<const uint4*>(mod + (size_t)st * 3 * W);
-  const uint4* scale = reinterpret_cast<const uint4*>(mod + (size_t)st * 3 * W + W);
   uint4* orow = reinterpret_cast<uint4*>(out + (size_t)row * W);
   uint4 ob[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
-    const uint4 sh = shift[lane + 64 * i], sc = scale[lane + 64 * i];
+    const uint4 sh = shv[i], sc = scv[i];
     const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
     const uint32_t a[4] = {sh.x, sh.y, sh.z, sh.w};
     const uint32_t b[4] = {sc.x, sc.y, sc.z, sc.w};

@@ -406,7 +406,10 @@ __device__ __forceinline__ void epilogue_qk224(const GemmArgs& g,
 #pragma unroll
       for (int r = 0; r < 16; ++r) a = fmaf(acc[i][j][r], acc[i][j][r], a);
     ss[i] = a + __shfl_xor(a, 32, 64);
-    if (hl == 0) s_rs[wn * BM + i * 32 + ln] = ss[i];
+    // both half-waves hold the same sum and store it to the same address: a
+    // store predicated on one half-wave let the compiler place a register
+    // copy inside its exec mask, which the other half then read stale
+    s_rs[wn * BM + i * 32 + ln] = ss[i];
   }
   __syncthreads();  // every wave of the tile is a q or k wave
 #pragma unroll

@@ -226,7 +226,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void thin_kernel(ThinArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) ss = fmaf(acc[i][r], acc[i][r], ss);
         ss += __shfl_xor(ss, 32, 64);
-        if (hl == 0) s_ss[wave][32 * i + ln] = ss;
+        s_ss[wave][32 * i + ln] = ss;  // both half-waves: same sum, same address
       }
       uint2 gsc[4];
 #pragma unroll

@@ -291,6 +291,24 @@ __global__ __launch_bounds__(64 * NWV, 1) void thin_kernel(ThinArgs g) {
       }
     }
   } else {
+    // y = x + gate_s r (flags: bit 0 no residual, bit 1 no gate).  The gate
+    // and residual are loaded before the pieces count themselves in, so the
+    // last to arrive (the launch's tail) does not wait for them after its sum.
+    const bool use_gate = !(g.flags & 2u), use_res = !(g.flags & 1u);
+    const int c0 = cb * BNW + 32 * wave + 4 * hl;
+    uint2 gv[MB][4], xv[MB][4];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int t = min(32 * i + ln, g.M - 1);
+      const uint16_t* gate = g.mod + (size_t)stream_of(t, g.e0, g.e1) * 3 * g.D + 2 * g.D + c0;
+      const uint16_t* xr = g.x + (size_t)t * g.D + c0;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        gv[i][rr] = use_gate ? *reinterpret_cast<const uint2*>(gate + 8 * rr)
+                             : make_uint2(0x3f803f80u, 0x3f803f80u);
+        xv[i][rr] = use_res ? *reinterpret_cast<const uint2*>(xr + 8 * rr) : make_uint2(0u, 0u);
+      }
+    }
     if (g.pieces > 1) {
       // Partials: slot (cb, piece), 4 waves x MB x 4 groups of 16 B x 64
       // lanes, lane-fastest so a wave store moves 1 KB.  The pieces of a
@@ -354,30 +372,18 @@ __global__ __launch_bounds__(64 * NWV, 1) void thin_kernel(ThinArgs g) {
 #pragma unroll
       for (int i = 0; i < MB; ++i) acc[i] = sum[i];
     }
-    // y = x + gate_s r (flags: bit 0 no residual, bit 1 no gate)
-    const bool use_gate = !(g.flags & 2u), use_res = !(g.flags & 1u);
-    const int c0 = cb * BNW + 32 * wave + 4 * hl;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int t = 32 * i + ln;
       if (t >= g.M) continue;
-      const uint16_t* gate = g.mod + (size_t)stream_of(t, g.e0, g.e1) * 3 * g.D + 2 * g.D + c0;
-      const uint16_t* xr = g.x + (size_t)t * g.D + c0;
       uint16_t* yr = g.y + (size_t)t * g.D + c0;
-      uint2 gv[4], xv[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        gv[rr] = use_gate ? *reinterpret_cast<const uint2*>(gate + 8 * rr)
-                          : make_uint2(0x3f803f80u, 0x3f803f80u);
-        xv[rr] = use_res ? *reinterpret_cast<const uint2*>(xr + 8 * rr) : make_uint2(0u, 0u);
-      }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
         *reinterpret_cast<uint2*>(yr + 8 * rr) =
-            pack4f(fmaf(lo2f(gv[rr].x), acc[i][4 * rr], lo2f(xv[rr].x)),
-                   fmaf(hi2f(gv[rr].x), acc[i][4 * rr + 1], hi2f(xv[rr].x)),
-                   fmaf(lo2f(gv[rr].y), acc[i][4 * rr + 2], lo2f(xv[rr].y)),
-                   fmaf(hi2f(gv[rr].y), acc[i][4 * rr + 3], hi2f(xv[rr].y)));
+            pack4f(fmaf(lo2f(gv[i][rr].x), acc[i][4 * rr], lo2f(xv[i][rr].x)),
+                   fmaf(hi2f(gv[i][rr].x), acc[i][4 * rr + 1], hi2f(xv[i][rr].x)),
+                   fmaf(lo2f(gv[i][rr].y), acc[i][4 * rr + 2], lo2f(xv[i][rr].y)),
+                   fmaf(hi2f(gv[i][rr].y), acc[i][4 * rr + 3], hi2f(xv[i][rr].y)));
     }
   }
 }

@@ -54,6 +54,17 @@
 //    waits for another, and the merge is symmetric in the two parts, so the
 //    result does not depend on which arrives first.  With at most as many
 //    items as CUs (or no scratch) each workgroup runs one whole item.
+//  * Whole-item rounds.  With at least two rounds of items, only the last
+//    round and the remainder (between one and two rounds) are split into
+//    shares; before that every workgroup runs whole items round by round,
+//    workgroup w taking item round * G + w.  Shares that start part-way
+//    through an item put each CU at its own key position, so on a long
+//    sequence every CU streamed its head's K and V on its own (52 GB from
+//    behind L2 per launch at 32,928 tokens, where one head's K and V are
+//    17 MB against a 4 MB L2); in whole-item rounds the 32 CUs of an XCD
+//    start together on consecutive query tiles of one head and read each
+//    key tile at about the same time.  Sequences of at most two rounds
+//    (4,256 tokens: 1.59) are split as before.
 //  * Shares of neighbouring workgroups sit on one XCD (and so do the items of
 //    one head), so K and V and the split partials stay in that XCD's L2.
 #include "common.h"
@@ -147,8 +158,15 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(
   // (gridDim.x == nqt * H) every share is exactly one whole item.
   const int G = gridDim.x;
   const int r = xcd_remap(blockIdx.x, G);
-  const long long total = (long long)nqt * H * ntiles;
-  const long long b0 = total * r / G, b1 = total * (r + 1) / G;
+  const int items = nqt * H;
+  // R whole-item rounds first (none with one workgroup per item, G = items),
+  // then the share [b0, b1) of the iterations after them
+  const int R = items >= 2 * G ? items / G - 1 : 0;
+  const long long split_from = (long long)R * G * ntiles;
+  const long long total = (long long)items * ntiles;
+  const long long b0 = split_from + (total - split_from) * r / G;
+  const long long b1 = split_from + (total - split_from) * (r + 1) / G;
+  const long long whole = (long long)R * ntiles;  // iterations of the whole-item rounds
 
   // Per-segment state read by the loops below: the head's K and V, the first
   // key tile kt0 and tile count nt of the segment, and the number of keys
@@ -517,19 +535,28 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void attn_fwd_kernel(
     }
   };
 
-  // The share, one segment (an item or the part of one inside the share) at
-  // a time.
-  for (long long at = b0; at < b1;) {
-    const long long seg_start = at;
-    const int item = (int)(at / ntiles);
-    const int k0 = (int)(at - (long long)item * ntiles);
-    const int k1 = (int)min((long long)ntiles, b1 - (long long)item * ntiles);
-    at = (long long)item * ntiles + k1;
+  // The whole-item rounds, then the share, one segment (an item or the part
+  // of one inside the share) at a time.  `done` counts this workgroup's
+  // iterations: [0, whole) the whole-item rounds, then the share.
+  for (long long done = 0; done < whole + (b1 - b0);) {
+    const long long seg_start = done;
+    int item, k0, k1;
+    if (done < whole) {
+      item = (int)(done / ntiles) * G + r;
+      k0 = 0;
+      k1 = ntiles;
+    } else {
+      const long long at = b0 + (done - whole);
+      item = (int)(at / ntiles);
+      k0 = (int)(at - (long long)item * ntiles);
+      k1 = (int)min((long long)ntiles, b1 - (long long)item * ntiles);
+    }
+    done += k1 - k0;
     const int h = item / nqt, qt = item % nqt;
     const int q0 = qt * BQ + wave * 32;
     // every wave is done with the previous segment's LDS tiles before the
     // rings are refilled
-    if (seg_start != b0) __syncthreads();
+    if (seg_start != 0) __syncthreads();
     kbase = reinterpret_cast<const char*>(k + (size_t)h * HD);
     vbase = reinterpret_cast<const char*>(v + (size_t)h * HD);
     kt0 = k0;

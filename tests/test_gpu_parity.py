@@ -128,11 +128,15 @@ def test_attn_parity_sampled(N, logit_std):
 # cut, checked on every row), 4,256 x 24 = 408 items (the block's shape),
 # 8,352 x 24 = 792, and 16,484 tokens x 4 heads = 260 items of 258 key tiles
 # against shares of 262 (every share holds the tail of one item and the head
-# of the next).  logit_std 1 to 8 runs the running-max merge with references
-# far apart.
+# of the next).  With at least two rounds of items the kernel first runs whole
+# items round by round: 8,352 x 24 (two whole rounds, then 280 items in
+# shares) and 2,100 tokens x 64 heads = 576 items (one whole round, then 320
+# items in 256 shares, checked on every row).  logit_std 1 to 8 runs the
+# running-max merge with references far apart.
 @pytest.mark.parametrize("N,H,logit_std,all_rows", [(3000, 24, 2.0, True), (4256, 24, 1.0, False),
                                                     (4256, 24, 8.0, False),
                                                     (8352, 24, 2.0, False),
+                                                    (2100, 64, 2.0, True),
                                                     (16484, 4, 4.0, False)])
 def test_attn_ws_split_parity(N, H, logit_std, all_rows):
     d = inputs.make_attn_inputs(N, H, 128, seed=8, logit_std=logit_std)

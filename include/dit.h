@@ -179,7 +179,9 @@ int dit_attn_workspace_bytes(int32_t n_tokens, int32_t n_heads, int32_t head_dim
  * CUs the way the block's attention does: when there are more (head, 256-query)
  * items than CUs, each CU takes an equal share of the key tiles of all
  * items, and an item cut between two shares is merged from two fp32
- * partials kept in the workspace.  Same result definition and errors as
+ * partials kept in the workspace.  With two or more rounds of items, all
+ * but the last round and the remainder run as whole items first, one per CU
+ * per round, and only the rest is shared out.  Same result definition and errors as
  * dit_attn_fwd, plus DIT_ERR_WORKSPACE (null or too small) and DIT_ERR_ARG
  * (workspace overlapping q, k, v or o). */
 int dit_attn_fwd_ws(int32_t n_tokens, int32_t n_heads, int32_t head_dim, const void* q,

@@ -1041,10 +1041,12 @@ Plan make_plan(int bm, int M, int KT, int num_n, bool can_split) {
     p.n_dp = full * cus;
     p.n_tail = tail;
     p.n_pieces = min(min(cus, kMaxPieces), tail * upt);
-    // the longest piece, plus partial stores and the fix-up pass
+    // the longest piece, plus partial stores and the fix-up pass, which
+    // grows with the tiles it sums (measured: 6.5 us for 4 bf16 224-row
+    // tiles, 14.4 us for 44 FP8 256-row ones, about 0.12 and 0.3 tile times)
     const int units = tail * upt;
     const int longest = (units + p.n_pieces - 1) / p.n_pieces;
-    p.cost = tile_time * (full + (float)longest / upt + 0.1f);
+    p.cost = tile_time * (full + (float)longest / upt + 0.1f + 0.005f * tail);
   } else {
     p.n_dp = p.tiles;
     p.n_tail = 0;

@@ -1020,7 +1020,7 @@ struct Plan {
   float cost;  // estimated time in tile times
 };
 
-Plan make_plan(int bm, int M, int KT, int num_n, bool can_split) {
+Plan make_plan(int bm, int M, int KT, int num_n, bool can_split, float fix_per_tile) {
   const int cus = device_cus();
   Plan p{};
   p.bm = bm;
@@ -1042,11 +1042,10 @@ Plan make_plan(int bm, int M, int KT, int num_n, bool can_split) {
     p.n_tail = tail;
     p.n_pieces = min(min(cus, kMaxPieces), tail * upt);
     // the longest piece, plus partial stores and the fix-up pass, which
-    // grows with the tiles it sums (measured: 6.5 us for 4 bf16 224-row
-    // tiles, 14.4 us for 44 FP8 256-row ones, about 0.12 and 0.3 tile times)
+    // grows with the tiles it sums by fix_per_tile tile times each
     const int units = tail * upt;
     const int longest = (units + p.n_pieces - 1) / p.n_pieces;
-    p.cost = tile_time * (full + (float)longest / upt + 0.1f + 0.005f * tail);
+    p.cost = tile_time * (full + (float)longest / upt + 0.1f + fix_per_tile * tail);
   } else {
     p.n_dp = p.tiles;
     p.n_tail = 0;
@@ -1072,19 +1071,28 @@ Plan make_plan(int bm, int M, int KT, int num_n, bool can_split) {
 // sequences they were measured slower than 224-row tiles (336 tokens, output
 // projection: more tiles with the same fixed costs each).
 template <class Ok>
-Plan pick_plan(int M, int KT, int num_n, bool can_split, bool allow128, Ok ok) {
+Plan pick_plan(int M, int KT, int num_n, bool can_split, bool allow128, float fix_per_tile, Ok ok) {
   auto plan = [&](int bm) {
-    const Plan p = make_plan(bm, M, KT, num_n, can_split);
-    return ok(p) ? p : make_plan(bm, M, KT, num_n, false);
+    const Plan p = make_plan(bm, M, KT, num_n, can_split, fix_per_tile);
+    return ok(p) ? p : make_plan(bm, M, KT, num_n, false, fix_per_tile);
   };
   const Plan a = plan(224), b = plan(256);
   Plan best = a.cost <= b.cost ? a : b;
   if (allow128 && can_split && M <= 128) {
-    const Plan c = make_plan(128, M, KT, num_n, true);
+    const Plan c = make_plan(128, M, KT, num_n, true, fix_per_tile);
     if (c.n_dp == 0 && c.n_tail > 0 && ok(c) && c.cost < best.cost) best = c;
   }
   return best;
 }
+
+// Fix-up cost per split tail tile, in tile times.  FP8: 14.4 us for the 44
+// tail tiles of the 4,256-token input projection with 256-row tiles, about
+// 0.3 of its tile time; with it that projection takes 224-row tiles (4 tail
+// tiles), measured 350 against 363 us.  bf16: the plans were tuned and
+// measured with the fix-up as a flat 0.1 (its per-tile cost, about 0.003,
+// would only flip near-ties that were not measured).
+template <bool F8>
+constexpr float kFixPerTile = F8 ? 0.007f : 0.0f;
 
 template <int EPI, bool F8>
 hipError_t launch(GemmArgs g, hipStream_t stream) {
@@ -1097,7 +1105,7 @@ hipError_t launch(GemmArgs g, hipStream_t stream) {
     // normalize or rotate, so a tail must hold no q or k tile (tail tiles are
     // the last in tile order, i.e. the highest N tiles: MLP ones).
     const int num_qk = 2 * g.D / BN;
-    p = pick_plan(g.M, g.KT, g.num_n, can_split, !F8, [&](const Plan& q) {
+    p = pick_plan(g.M, g.KT, g.num_n, can_split, !F8, kFixPerTile<F8>, [&](const Plan& q) {
       const int num_m = (g.M + q.bm - 1) / q.bm;
       return !(q.n_tail && q.n_dp > 0 && (q.n_dp / (GROUP_N * num_m)) * GROUP_N < num_qk);
     });
@@ -1105,7 +1113,8 @@ hipError_t launch(GemmArgs g, hipStream_t stream) {
     // norm + RoPE pass runs on them afterwards
     qk_after = p.n_tail > 0 && p.n_dp == 0;
   } else {
-    p = pick_plan(g.M, g.KT, g.num_n, can_split, !F8, [](const Plan&) { return true; });
+    p = pick_plan(g.M, g.KT, g.num_n, can_split, !F8, kFixPerTile<F8>,
+                  [](const Plan&) { return true; });
   }
   g.n_dp = p.n_dp;
   g.n_tail = p.n_tail;
